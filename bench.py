@@ -1,0 +1,324 @@
+#!/usr/bin/env python3
+"""Benchmark of the MoE expert-parallel hot path on one MI355X.
+
+One step = moe_layout + moe_dispatch + moe_combine over one batch of synthetic
+input already resident in HBM.  The default workload is the prefill shape
+(S=4096 tokens, H=7168, E=256 experts in 8 groups, top-4 groups / top-8
+experts, R=8 simulated ranks, FP8 E4M3 dispatch with per-128-channel fp32
+scales, bf16 combine).  Prints one JSON line.
+
+Timing: W untimed warm-up steps, then K timed steps bracketed by
+torch.cuda.synchronize(); HIP events on the launch stream around every call
+give per-kernel averages.  Bytes are the algorithmic bytes the path must move
+(padding rows excluded), GB = 1e9.
+
+  --gpus N           only N=1 exists: the EP ranks are partitions of one buffer
+  --config NAME      tiny | prefill | decode | skew | dsmoe16b
+  --calib-copy       run only a plain device copy of known size (for scaling
+                     rocprofv3 FETCH_SIZE / WRITE_SIZE counters)
+  --no-cpu-baseline  skip timing the CPU oracle
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "dispatch+combine HBM GB/s (% of peak) at S=4096,H=7168,E=256,K=8; µs at S=128"
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, 8 TB/s
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+# ---------------------------------------------------------------------------
+# byte accounting
+# ---------------------------------------------------------------------------
+
+def row_bytes(H: int, fp8: bool) -> int:
+    """Bytes of one dispatched row: bf16 payload, or E4M3 codes plus one fp32
+    scale per 128 channels."""
+    return H + 4 * (H // 128) if fp8 else 2 * H
+
+
+def message_bytes(S: int, K: int, H: int, fp8: bool, combine: bool) -> int:
+    """Payload bytes of one dispatch or combine, counted one message per
+    (token, k) entry: the convention that reproduces the GB/s column of
+    DeepEP's low-latency benchmark table from its latency column."""
+    return S * K * (2 * H if combine else row_bytes(H, fp8))
+
+
+def layout_bytes(S: int, K: int, max_recv: int) -> int:
+    # read topk_idx, write pos, write src
+    return 8 * S * K + 4 * max_recv
+
+
+def dispatch_bytes(S: int, K: int, H: int, fp8: bool, placed: int) -> int:
+    # read hidden once; write every placed row (+ scales); pos, weight, recv_w per entry
+    return 2 * S * H + placed * row_bytes(H, fp8) + 12 * S * K
+
+
+def combine_bytes(S: int, K: int, H: int, placed: int, shared: bool) -> int:
+    # gather every placed row, pos + weight per entry, write out (+ read shared)
+    return placed * 2 * H + 8 * S * K + 2 * S * H + (2 * S * H if shared else 0)
+
+
+# ---------------------------------------------------------------------------
+
+def file_sha256(path: str) -> str:
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def load_traffic(kernel_src: str, workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter runs, or None
+    when the kernel source changed since they were taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    entry = rec.get(workload)
+    if not entry or entry.get("source_sha256") != file_sha256(kernel_src):
+        return None
+    return entry.get("bytes_per_launch")
+
+
+class Run:
+    """Device buffers and launches of one workload."""
+
+    def __init__(self, moe, cfg, dev, seed=None):
+        import numpy as np
+        import torch
+        from workloads import make_workload
+        self.cfg = cfg
+        self.moe = moe
+        w = make_workload(cfg, seed=seed)
+        self.w = w
+        self.desc = moe.LayoutDesc(cfg.S, cfg.K, cfg.E, cfg.R, cfg.pad_mode, cfg.pad_rows)
+        self.rows = moe.moe_max_recv_rows(self.desc)
+        self.idx = torch.from_numpy(w.topk_idx).to(dev)
+        self.hidden = torch.from_numpy(w.hidden.view(np.int16)).to(dev).view(torch.bfloat16)
+        self.topk_w = torch.from_numpy(w.topk_w).to(dev)
+        self.shared = (torch.from_numpy(w.shared.view(np.int16)).to(dev).view(torch.bfloat16)
+                       if w.shared is not None else None)
+        self.layout = moe.alloc_layout(self.desc, dev)
+        H = cfg.H
+        if cfg.fp8:
+            self.recv = torch.empty((self.rows, H), dtype=torch.uint8, device=dev)
+            self.scales = torch.empty((self.rows, H // 128), dtype=torch.float32, device=dev)
+        else:
+            self.recv = torch.empty((self.rows, H), dtype=torch.bfloat16, device=dev)
+            self.scales = None
+        self.recv_w = torch.empty(self.rows, dtype=torch.float32, device=dev)
+        # stand-in expert outputs: seeded N(0,1) bf16 for every row
+        g = torch.Generator(device=dev)
+        g.manual_seed(w.seed)
+        self.expert_out = torch.randn((self.rows, H), generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+        self.out = torch.empty((cfg.S, H), dtype=torch.bfloat16, device=dev)
+        self.placed = None
+
+    def layout_call(self):
+        self.moe.moe_layout(self.desc, self.idx, self.layout)
+
+    def dispatch_call(self):
+        self.moe.moe_dispatch(self.desc, self.layout, self.hidden, self.idx, self.topk_w, fp8=self.cfg.fp8,
+                              recv=self.recv, recv_scales=self.scales, recv_w=self.recv_w)
+
+    def combine_call(self):
+        self.moe.moe_combine(self.desc, self.layout, self.expert_out, self.topk_w, self.shared, out=self.out)
+
+    def step(self):
+        self.layout_call()
+        self.dispatch_call()
+        self.combine_call()
+
+    def bytes(self):
+        import torch
+        if self.placed is None:
+            torch.cuda.synchronize()
+            self.placed = int(self.layout.tokens_per_expert.sum().item())
+        c = self.cfg
+        return (layout_bytes(c.S, c.K, self.rows),
+                dispatch_bytes(c.S, c.K, c.H, c.fp8, self.placed),
+                combine_bytes(c.S, c.K, c.H, self.placed, c.shared))
+
+
+def time_steps(run, steps: int, warmup: int):
+    """Per-call averages (ms) from HIP events on the launch stream, plus the
+    wall time of the whole timed region."""
+    import torch
+    for _ in range(warmup):
+        run.step()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        ev[i][0].record()
+        run.layout_call()
+        ev[i][1].record()
+        run.dispatch_call()
+        ev[i][2].record()
+        run.combine_call()
+        ev[i][3].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    lay = sum(e[0].elapsed_time(e[1]) for e in ev) / steps
+    dis = sum(e[1].elapsed_time(e[2]) for e in ev) / steps
+    com = sum(e[2].elapsed_time(e[3]) for e in ev) / steps
+    span = ev[0][0].elapsed_time(ev[-1][3]) / steps
+    return dict(layout_ms=lay, dispatch_ms=dis, combine_ms=com, step_ms=span, wall_s=wall)
+
+
+def time_graph(run, iters: int):
+    """Layout + dispatch + combine captured once in a HIP graph, replayed."""
+    import torch
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        run.step()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        run.step()
+    for _ in range(10):
+        graph.replay()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(iters):
+        graph.replay()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / iters
+
+
+def cpu_baseline(cfg, budget_s: float = 12.0):
+    """The CPU oracle (single-threaded C) on the same workload: layout, dispatch
+    and combine of full batches, repeated until ~budget_s of work."""
+    import numpy as np
+    import oracle
+    from workloads import make_workload, random_expert_out_bits
+    w = make_workload(cfg)
+    rows = oracle.max_recv_rows(cfg.S, cfg.K, cfg.E, cfg.R, cfg.pad_mode, cfg.pad_rows)
+    y = random_expert_out_bits(w.seed, rows, cfg.H)
+    passes, t_total, nbytes = 0, 0.0, 0
+    while t_total < budget_s or passes == 0:
+        t0 = time.perf_counter()
+        lo = oracle.layout(w.topk_idx, cfg.E, cfg.R, cfg.pad_mode, cfg.pad_rows)
+        if cfg.fp8:
+            oracle.dispatch_fp8(w.hidden, lo.pos, rows, w.topk_w)
+        else:
+            oracle.dispatch_bf16(w.hidden, lo.pos, rows, w.topk_w)
+        oracle.combine(y, lo.pos, w.topk_w, w.shared)
+        t_total += time.perf_counter() - t0
+        passes += 1
+        placed = int(lo.tokens_per_expert.sum())
+        nbytes += (layout_bytes(cfg.S, cfg.K, rows) + dispatch_bytes(cfg.S, cfg.K, cfg.H, cfg.fp8, placed)
+                   + combine_bytes(cfg.S, cfg.K, cfg.H, placed, cfg.shared))
+        del lo
+    return {"value": round(nbytes / t_total / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{passes} full {cfg.name} batches (S={cfg.S}, layout + "
+                      f"{'fp8' if cfg.fp8 else 'bf16'} dispatch + combine), {t_total:.1f} s single-threaded",
+            "ms_per_step": round(1e3 * t_total / passes, 2), "host_cpus": os.cpu_count()}
+
+
+def calib_copy(nbytes: int = 1 << 30):
+    """A plain device-to-device copy of a known size, for counter scaling."""
+    import torch
+    a = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda:0").fill_(1.0)
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"calib_copy_bytes": nbytes, "launches": 3}))
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", default="prefill")
+    ap.add_argument("--decode-iters", type=int, default=500)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--calib-copy", action="store_true")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the EP ranks are simulated as partitions of one HBM buffer, "
+              "so --gpus must be 1", file=sys.stderr)
+        sys.exit(2)
+    if args.calib_copy:
+        calib_copy()
+        return
+
+    import torch
+    import combine_moe_layout_02_amd as moe
+    from workloads import CONFIGS
+
+    dev = torch.device("cuda:0")
+    cfg = CONFIGS[args.config]
+    run = Run(moe, cfg, dev)
+    lb, db, cb = run.bytes()
+    t = time_steps(run, args.steps, args.warmup)
+    step_bytes = lb + db + cb
+    value = step_bytes / (t["step_ms"] * 1e-3) / 1e9
+    d_gbps = db / (t["dispatch_ms"] * 1e-3) / 1e9
+    c_gbps = cb / (t["combine_ms"] * 1e-3) / 1e9
+    dc_gbps = (db + cb) / ((t["dispatch_ms"] + t["combine_ms"]) * 1e-3) / 1e9
+
+    # dominant kernel: the larger byte mover of dispatch and combine
+    dom = "combine" if cb >= db else "dispatch"
+    dom_bytes, dom_ms = (cb, t["combine_ms"]) if dom == "combine" else (db, t["dispatch_ms"])
+    achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
+    src = os.path.join(ROOT, "combine_moe_layout_02_amd", "csrc", f"{dom}.hip")
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": load_traffic(src, f"{dom}/{cfg.name}"),
+                "kernel": dom, "algorithmic_bytes_per_launch": dom_bytes,
+                "avg_launch_us": round(dom_ms * 1e3, 2)}
+
+    extra = {"layout_us": round(t["layout_ms"] * 1e3, 2), "dispatch_us": round(t["dispatch_ms"] * 1e3, 2),
+             "combine_us": round(t["combine_ms"] * 1e3, 2), "dispatch_gbps": round(d_gbps, 1),
+             "combine_gbps": round(c_gbps, 1), "dispatch_plus_combine_gbps": round(dc_gbps, 1),
+             "dispatch_plus_combine_frac_of_peak": round(dc_gbps / HBM_PEAK_GBPS, 4),
+             "bytes": {"layout": lb, "dispatch": db, "combine": cb}, "wall_s_timed": round(t["wall_s"], 3)}
+
+    decode = None
+    if not args.no_decode:
+        dcfg = CONFIGS["decode"]
+        drun = Run(moe, dcfg, dev)
+        dt = time_steps(drun, args.decode_iters, 20)
+        g_ms = time_graph(drun, args.decode_iters)
+        decode = {"us_per_call": round(dt["step_ms"] * 1e3, 2), "layout_us": round(dt["layout_ms"] * 1e3, 2),
+                  "dispatch_us": round(dt["dispatch_ms"] * 1e3, 2), "combine_us": round(dt["combine_ms"] * 1e3, 2),
+                  "graph_replay_us_per_call": round(g_ms * 1e3, 2),
+                  "config": {"workload": "decode", "S": dcfg.S, "H": dcfg.H, "E": dcfg.E, "K": dcfg.K,
+                             "R": dcfg.R, "fp8": True, "capacity": dcfg.pad_rows}}
+        del drun
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(cfg)
+
+    line = {
+        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(t["step_ms"], 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": cfg.name, "S": cfg.S, "H": cfg.H, "E": cfg.E, "K": cfg.K, "R": cfg.R,
+                   "fp8_dispatch": cfg.fp8, "routing": cfg.routing, "pad_mode": cfg.pad_mode,
+                   "pad_rows": cfg.pad_rows, "shared": cfg.shared, "parallelism": "ep8 simulated on 1 GPU"},
+        "roofline": roofline, "cpu_baseline": cpu, "kernels": extra, "decode": decode,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

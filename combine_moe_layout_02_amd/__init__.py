@@ -1,0 +1,232 @@
+"""MI355X-native MoE expert-parallel layout, dispatch and combine.
+
+Thin ctypes binding over libmoe_ep.so (declared in include/moe_ep.h).  The
+Python functions carry the C names and only marshal arguments: torch tensors
+supply device memory and the current HIP stream, every step of the path runs
+in the library's HIP kernels.  Importing this package fails loudly when the
+library has not been built; there is no CPU fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+import os
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmoe_ep.so")
+
+MOE_OK, MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_ALIGN, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(6)
+MOE_PAD_NONE, MOE_PAD_MULTIPLE, MOE_PAD_CAPACITY = 0, 1, 2
+MOE_FLAG_BAD_EXPERT, MOE_FLAG_CAPACITY = 1, 2
+
+EXPORTED = ("moe_max_recv_rows", "moe_layout_workspace_bytes", "moe_layout", "moe_dispatch",
+            "moe_combine", "moe_status_str")
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status: int, call: str):
+        self.status = status
+        super().__init__(f"{call}: {_lib.moe_status_str(status).decode()}")
+
+
+class moe_layout_desc(ctypes.Structure):
+    _fields_ = [("S", ctypes.c_int32), ("K", ctypes.c_int32), ("E", ctypes.c_int32),
+                ("R", ctypes.c_int32), ("pad_mode", ctypes.c_int32), ("pad_rows", ctypes.c_int32)]
+
+
+class moe_layout_bufs(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in ("tokens_per_expert", "tokens_per_rank", "expert_offset",
+                                               "rank_offset", "pos", "src", "status")]
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with `python -c 'import __graft_entry__ as g; "
+                          "g.build()'` (hipcc, gfx950); there is no fallback path")
+    L = ctypes.CDLL(LIB_PATH)
+    P = ctypes.c_void_p
+    D = ctypes.POINTER(moe_layout_desc)
+    B = ctypes.POINTER(moe_layout_bufs)
+    L.moe_max_recv_rows.argtypes = [D]
+    L.moe_max_recv_rows.restype = ctypes.c_int64
+    L.moe_layout_workspace_bytes.argtypes = [D]
+    L.moe_layout_workspace_bytes.restype = ctypes.c_size_t
+    L.moe_layout.argtypes = [D, P, B, P, ctypes.c_size_t, P]
+    L.moe_layout.restype = ctypes.c_int
+    L.moe_dispatch.argtypes = [D, B, P, ctypes.c_int32, P, P, ctypes.c_int32, P, P, P, P]
+    L.moe_dispatch.restype = ctypes.c_int
+    L.moe_combine.argtypes = [D, B, P, ctypes.c_int32, P, P, P, P]
+    L.moe_combine.restype = ctypes.c_int
+    L.moe_status_str.argtypes = [ctypes.c_int32]
+    L.moe_status_str.restype = ctypes.c_char_p
+    return L
+
+
+_lib = _load()
+
+
+def lib() -> ctypes.CDLL:
+    return _lib
+
+
+# ---------------------------------------------------------------------------
+# descriptors
+# ---------------------------------------------------------------------------
+
+@dataclasses.dataclass(frozen=True)
+class LayoutDesc:
+    S: int
+    K: int
+    E: int
+    R: int
+    pad_mode: int = MOE_PAD_NONE
+    pad_rows: int = 0
+
+    def c(self) -> moe_layout_desc:
+        return moe_layout_desc(self.S, self.K, self.E, self.R, self.pad_mode, self.pad_rows)
+
+
+@dataclasses.dataclass
+class Layout:
+    """Device tensors of one batch's layout (outputs of moe_layout)."""
+    tokens_per_expert: torch.Tensor   # [E] int32
+    tokens_per_rank: torch.Tensor     # [R] int32
+    expert_offset: torch.Tensor       # [E+1] int32
+    rank_offset: torch.Tensor         # [R+1] int32
+    pos: torch.Tensor                 # [S,K] int32
+    src: torch.Tensor                 # [max_recv] int32
+    status: torch.Tensor              # [1] int32
+    workspace: Optional[torch.Tensor] = None
+
+    def c(self) -> moe_layout_bufs:
+        return moe_layout_bufs(*(t.data_ptr() for t in (
+            self.tokens_per_expert, self.tokens_per_rank, self.expert_offset, self.rank_offset,
+            self.pos, self.src, self.status)))
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream, device) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _check(t: Optional[torch.Tensor], name: str, dtype, shape=None, device=None):
+    if t is None:
+        return
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if dtype is not None and t.dtype not in (dtype if isinstance(dtype, tuple) else (dtype,)):
+        raise TypeError(f"{name}: dtype {t.dtype}, expected {dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+
+
+# ---------------------------------------------------------------------------
+# the C calls
+# ---------------------------------------------------------------------------
+
+def moe_max_recv_rows(desc: LayoutDesc) -> int:
+    d = desc.c()
+    return int(_lib.moe_max_recv_rows(ctypes.byref(d)))
+
+
+def moe_layout_workspace_bytes(desc: LayoutDesc) -> int:
+    d = desc.c()
+    return int(_lib.moe_layout_workspace_bytes(ctypes.byref(d)))
+
+
+def moe_status_str(status: int) -> str:
+    return _lib.moe_status_str(int(status)).decode()
+
+
+def alloc_layout(desc: LayoutDesc, device) -> Layout:
+    """Device buffers for moe_layout's outputs and its workspace (torch memory)."""
+    rows = moe_max_recv_rows(desc)
+    if rows < 0:
+        raise MoeError(MOE_ERR_SHAPE, "alloc_layout")
+    i32 = dict(dtype=torch.int32, device=device)
+    ws = moe_layout_workspace_bytes(desc)
+    return Layout(
+        tokens_per_expert=torch.empty(desc.E, **i32), tokens_per_rank=torch.empty(desc.R, **i32),
+        expert_offset=torch.empty(desc.E + 1, **i32), rank_offset=torch.empty(desc.R + 1, **i32),
+        pos=torch.empty((desc.S, desc.K), **i32), src=torch.empty(rows, **i32),
+        status=torch.empty(1, **i32),
+        workspace=torch.empty(ws, dtype=torch.uint8, device=device) if ws else None)
+
+
+def moe_layout(desc: LayoutDesc, topk_idx: torch.Tensor, layout: Optional[Layout] = None,
+               stream=None) -> Layout:
+    dev = topk_idx.device
+    _check(topk_idx, "topk_idx", torch.int32, (desc.S, desc.K))
+    if layout is None:
+        layout = alloc_layout(desc, dev)
+    ws = layout.workspace
+    d, b = desc.c(), layout.c()
+    rc = _lib.moe_layout(ctypes.byref(d), _ptr(topk_idx), ctypes.byref(b), _ptr(ws),
+                         0 if ws is None else ws.numel(), _stream(stream, dev))
+    if rc != MOE_OK:
+        raise MoeError(rc, "moe_layout")
+    return layout
+
+
+def moe_dispatch(desc: LayoutDesc, layout: Layout, hidden: torch.Tensor, topk_idx=None, topk_w=None,
+                 fp8: bool = False, recv=None, recv_scales=None, recv_w=None, stream=None):
+    """Returns (recv, recv_scales or None, recv_w or None).  recv is bf16
+    [max_recv,H], or uint8 E4M3FN codes [max_recv,H] when fp8."""
+    dev = hidden.device
+    S, H = hidden.shape
+    rows = moe_max_recv_rows(desc)
+    _check(hidden, "hidden", torch.bfloat16, (desc.S, H))
+    _check(topk_w, "topk_w", torch.float32, (desc.S, desc.K))
+    if recv is None:
+        recv = torch.empty((rows, H), dtype=torch.uint8 if fp8 else torch.bfloat16, device=dev)
+    if fp8 and recv_scales is None:
+        recv_scales = torch.empty((rows, H // 128), dtype=torch.float32, device=dev)
+    if recv_w is None and topk_w is not None:
+        recv_w = torch.empty(rows, dtype=torch.float32, device=dev)
+    _check(recv, "recv", (torch.uint8, torch.float8_e4m3fn) if fp8 else torch.bfloat16)
+    if recv.shape[0] < rows or recv.shape[-1] != H:
+        raise ValueError("recv must hold moe_max_recv_rows rows of H channels")
+    if fp8:
+        _check(recv_scales, "recv_scales", torch.float32)
+        if recv_scales.shape[0] < rows or recv_scales.shape[-1] != H // 128:
+            raise ValueError("recv_scales must be [max_recv, H/128]")
+    _check(recv_w, "recv_w", torch.float32)
+    d, b = desc.c(), layout.c()
+    rc = _lib.moe_dispatch(ctypes.byref(d), ctypes.byref(b), _ptr(hidden), H, _ptr(topk_idx), _ptr(topk_w),
+                           1 if fp8 else 0, _ptr(recv), _ptr(recv_scales if fp8 else None), _ptr(recv_w),
+                           _stream(stream, dev))
+    if rc != MOE_OK:
+        raise MoeError(rc, "moe_dispatch")
+    return recv, (recv_scales if fp8 else None), recv_w
+
+
+def moe_combine(desc: LayoutDesc, layout: Layout, expert_out: torch.Tensor, w=None, shared_out=None,
+                out=None, stream=None) -> torch.Tensor:
+    dev = expert_out.device
+    H = expert_out.shape[-1]
+    _check(expert_out, "expert_out", torch.bfloat16)
+    if expert_out.shape[0] < moe_max_recv_rows(desc):
+        raise ValueError("expert_out must hold moe_max_recv_rows rows")
+    _check(w, "w", torch.float32, (desc.S, desc.K))
+    _check(shared_out, "shared_out", torch.bfloat16, (desc.S, H))
+    if out is None:
+        out = torch.empty((desc.S, H), dtype=torch.bfloat16, device=dev)
+    _check(out, "out", torch.bfloat16, (desc.S, H))
+    d, b = desc.c(), layout.c()
+    rc = _lib.moe_combine(ctypes.byref(d), ctypes.byref(b), _ptr(expert_out), H, _ptr(w), _ptr(shared_out),
+                          _ptr(out), _stream(stream, dev))
+    if rc != MOE_OK:
+        raise MoeError(rc, "moe_combine")
+    return out

@@ -1,0 +1,151 @@
+// C ABI front end of libmoe_ep.so: argument checks, launch-shape choice, and
+// status codes.  Declarations and the meaning of every argument are in
+// include/moe_ep.h.  Nothing here allocates, frees or synchronises.
+#include <stdint.h>
+
+#include "moe_ep.h"
+#include "moe_kernels.h"
+
+namespace {
+
+bool desc_ok(const moe_layout_desc *d) {
+    if (d->S < 0 || d->K < 1 || d->K > moe::kMaxK || d->E < 1 || d->E > moe::kMaxE || d->R < 1 ||
+        d->R > d->E || d->E % d->R != 0)
+        return false;
+    if (d->pad_mode != MOE_PAD_NONE && d->pad_mode != MOE_PAD_MULTIPLE && d->pad_mode != MOE_PAD_CAPACITY)
+        return false;
+    if (d->pad_mode != MOE_PAD_NONE && d->pad_rows < 1) return false;
+    if (static_cast<int64_t>(d->S) * d->K >= (int64_t(1) << 31)) return false;
+    return true;
+}
+
+int64_t max_rows(const moe_layout_desc *d) {
+    const int64_t n = static_cast<int64_t>(d->S) * d->K;
+    int64_t rows = n;
+    if (d->pad_mode == MOE_PAD_MULTIPLE) rows = n + static_cast<int64_t>(d->E) * (d->pad_rows - 1);
+    if (d->pad_mode == MOE_PAD_CAPACITY) rows = static_cast<int64_t>(d->E) * d->pad_rows;
+    return rows >= (int64_t(1) << 31) ? -1 : rows;
+}
+
+int ceil_log2(int x) {
+    int b = 0;
+    while ((1 << b) < x) ++b;
+    return b;
+}
+
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+}  // namespace
+
+extern "C" {
+
+int64_t moe_max_recv_rows(const moe_layout_desc *desc) {
+    if (desc == nullptr || !desc_ok(desc)) return -1;
+    return max_rows(desc);
+}
+
+size_t moe_layout_workspace_bytes(const moe_layout_desc *desc) {
+    if (desc == nullptr || !desc_ok(desc)) return 0;
+    return moe::layout_workspace_bytes(static_cast<int64_t>(desc->S) * desc->K, desc->E);
+}
+
+moe_status moe_layout(const moe_layout_desc *desc, const int32_t *topk_idx, const moe_layout_bufs *out,
+                      void *workspace, size_t workspace_bytes, void *stream) {
+    if (desc == nullptr || out == nullptr) return MOE_ERR_NULL;
+    if (!desc_ok(desc) || max_rows(desc) < 0) return MOE_ERR_SHAPE;
+    const int64_t n = static_cast<int64_t>(desc->S) * desc->K;
+    if (out->tokens_per_expert == nullptr || out->tokens_per_rank == nullptr ||
+        out->expert_offset == nullptr || out->rank_offset == nullptr || out->status == nullptr)
+        return MOE_ERR_NULL;
+    if (max_rows(desc) > 0 && out->src == nullptr) return MOE_ERR_NULL;
+    if (n > 0 && (topk_idx == nullptr || out->pos == nullptr)) return MOE_ERR_NULL;
+    const void *ints[] = {topk_idx, out->tokens_per_expert, out->tokens_per_rank, out->expert_offset,
+                          out->rank_offset, out->pos, out->src, out->status};
+    for (const void *p : ints)
+        if (!aligned(p, 4)) return MOE_ERR_ALIGN;
+    const size_t need = moe::layout_workspace_bytes(n, desc->E);
+    if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return MOE_ERR_WORKSPACE;
+    if (need > 0 && !aligned(workspace, 16)) return MOE_ERR_ALIGN;
+
+    moe::LayoutArgs a{};
+    a.idx = topk_idx;
+    a.N = static_cast<int32_t>(n);
+    a.E = desc->E;
+    a.R = desc->R;
+    a.pad_mode = desc->pad_mode;
+    a.pad_rows = desc->pad_rows;
+    a.nbits = ceil_log2(desc->E);
+    a.max_recv = static_cast<int32_t>(max_rows(desc));
+    a.tpe = out->tokens_per_expert;
+    a.tpr = out->tokens_per_rank;
+    a.eoff = out->expert_offset;
+    a.roff = out->rank_offset;
+    a.pos = out->pos;
+    a.src = out->src;
+    a.status = out->status;
+    a.blk_hist = static_cast<int32_t *>(workspace);
+    return moe::launch_layout(a, static_cast<hipStream_t>(stream)) == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+moe_status moe_dispatch(const moe_layout_desc *desc, const moe_layout_bufs *layout, const void *hidden,
+                        int32_t H, const int32_t *topk_idx, const float *topk_w, int32_t fp8, void *recv,
+                        float *recv_scales, float *recv_w, void *stream) {
+    (void)topk_idx;  // already folded into layout->pos
+    if (desc == nullptr || layout == nullptr) return MOE_ERR_NULL;
+    if (!desc_ok(desc) || max_rows(desc) < 0 || H < 8 || H % 8 != 0) return MOE_ERR_SHAPE;
+    if (fp8 && H % 128 != 0) return MOE_ERR_SHAPE;
+    if (desc->S == 0) return MOE_OK;
+    if (hidden == nullptr || recv == nullptr || layout->pos == nullptr) return MOE_ERR_NULL;
+    if (fp8 && recv_scales == nullptr) return MOE_ERR_NULL;
+    if (!aligned(hidden, 16) || !aligned(recv, 16) || !aligned(layout->pos, 4) || !aligned(recv_scales, 4) ||
+        !aligned(recv_w, 4) || !aligned(topk_w, 4))
+        return MOE_ERR_ALIGN;
+    moe::DispatchArgs a{};
+    a.hidden = hidden;
+    a.S = desc->S;
+    a.H = H;
+    a.K = desc->K;
+    a.pos = layout->pos;
+    a.topk_w = topk_w;
+    a.recv = recv;
+    a.recv_scales = recv_scales;
+    a.recv_w = recv_w;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    const hipError_t err = fp8 ? moe::launch_dispatch_fp8(a, s) : moe::launch_dispatch_bf16(a, s);
+    return err == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+moe_status moe_combine(const moe_layout_desc *desc, const moe_layout_bufs *layout, const void *expert_out,
+                       int32_t H, const float *w, const void *shared_out, void *out, void *stream) {
+    if (desc == nullptr || layout == nullptr) return MOE_ERR_NULL;
+    if (!desc_ok(desc) || max_rows(desc) < 0 || H < 8 || H % 8 != 0) return MOE_ERR_SHAPE;
+    if (desc->S == 0) return MOE_OK;
+    if (expert_out == nullptr || out == nullptr || layout->pos == nullptr) return MOE_ERR_NULL;
+    if (!aligned(expert_out, 16) || !aligned(out, 16) || !aligned(shared_out, 16) || !aligned(w, 4) ||
+        !aligned(layout->pos, 4))
+        return MOE_ERR_ALIGN;
+    moe::CombineArgs a{};
+    a.y = expert_out;
+    a.S = desc->S;
+    a.H = H;
+    a.K = desc->K;
+    a.pos = layout->pos;
+    a.w = w;
+    a.shared = shared_out;
+    a.out = out;
+    return moe::launch_combine(a, static_cast<hipStream_t>(stream)) == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+const char *moe_status_str(int32_t status) {
+    switch (status) {
+        case MOE_OK: return "MOE_OK";
+        case MOE_ERR_NULL: return "MOE_ERR_NULL: a required pointer is NULL";
+        case MOE_ERR_SHAPE: return "MOE_ERR_SHAPE: a size or mode is outside the supported limits";
+        case MOE_ERR_ALIGN: return "MOE_ERR_ALIGN: a buffer is not aligned as required";
+        case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE: workspace missing or too small";
+        case MOE_ERR_HIP: return "MOE_ERR_HIP: the HIP runtime refused a launch";
+        default: return "unknown moe_status";
+    }
+}
+
+}  // extern "C"

@@ -1,0 +1,117 @@
+// Combine kernel: bring each token's K expert-output rows back to token order
+// and merge them with the route weights, plus an optional shared-expert output.
+//
+// Results return from the experts and are merged per token (delect.ru glossary
+// "Expert parallelism (EP)", MOELayer.forward fact), in BF16 (DeepEP analysis,
+// both benchmark set-ups); DeepSeekMoE adds always-active shared experts next
+// to the routed ones (DeepEP analysis, "DeepSeek MoE": 2 shared + 64 routed
+// experts in the 16B model).
+//
+// out[t,c] = bf16_rne( fma-chain over k = 0..K-1 of w[t,k] * y[pos[t,k], c],
+//                      starting at +0.0, then + shared[t,c] ).
+// A lane owns 8 channels of one token: it issues all K 16-byte gathers before
+// the first fma (K loads in flight), keeps 8 fp32 accumulators, and writes one
+// 16-byte store.  The K row indices and weights are wave-uniform scalars.
+#include "moe_kernels.h"
+
+namespace moe {
+namespace {
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float bf16_lo(unsigned int w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(unsigned int w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// two fp32 -> packed bf16 pair, round to nearest even (v_cvt_pk_bf16_f32)
+__device__ __forceinline__ unsigned int pack_bf16x2(float lo, float hi) {
+    const f32x2 v = {lo, hi};
+    const bf16x2 b = __builtin_convertvector(v, bf16x2);
+    return __builtin_bit_cast(unsigned int, b);
+}
+
+inline int row_block(int nvec) {
+    if (nvec % 256 == 0) return 256;
+    if (nvec % 128 == 0) return 128;
+    if (nvec >= 256) return 256;
+    return ((nvec + 63) / 64) * 64;
+}
+
+template <int K>
+__global__ __launch_bounds__(256) void k_combine(CombineArgs a) {
+    const int t = blockIdx.x;
+    const int nvec = a.H / 8;
+    const int v = blockIdx.y * blockDim.x + threadIdx.x;
+    if (v >= nvec) return;
+    const u32x4 *__restrict__ y = static_cast<const u32x4 *>(a.y);
+    const int32_t *__restrict__ pos = a.pos + static_cast<size_t>(t) * K;
+
+    int p[K];
+    u32x4 r[K];
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+        p[k] = pos[k];
+        // an entry that was not placed reads row 0 and is then ignored
+        const size_t row = p[k] >= 0 ? static_cast<size_t>(p[k]) : 0;
+        r[k] = __builtin_nontemporal_load(y + row * nvec + v);
+    }
+    float acc[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+        const float wk = a.w != nullptr ? a.w[static_cast<size_t>(t) * K + k] : 1.0f;
+        const bool use = p[k] >= 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float c0 = __builtin_fmaf(wk, bf16_lo(r[k][i]), acc[2 * i]);
+            const float c1 = __builtin_fmaf(wk, bf16_hi(r[k][i]), acc[2 * i + 1]);
+            acc[2 * i] = use ? c0 : acc[2 * i];
+            acc[2 * i + 1] = use ? c1 : acc[2 * i + 1];
+        }
+    }
+    if (a.shared != nullptr) {
+        const u32x4 sh = __builtin_nontemporal_load(static_cast<const u32x4 *>(a.shared) +
+                                                     static_cast<size_t>(t) * nvec + v);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            acc[2 * i] = acc[2 * i] + bf16_lo(sh[i]);
+            acc[2 * i + 1] = acc[2 * i + 1] + bf16_hi(sh[i]);
+        }
+    }
+    u32x4 o;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) o[i] = pack_bf16x2(acc[2 * i], acc[2 * i + 1]);
+    __builtin_nontemporal_store(o, static_cast<u32x4 *>(a.out) + static_cast<size_t>(t) * nvec + v);
+}
+
+}  // namespace
+
+hipError_t launch_combine(const CombineArgs &a, hipStream_t s) {
+    const int nvec = a.H / 8;
+    const int bs = row_block(nvec);
+    const dim3 grid(a.S, (nvec + bs - 1) / bs), block(bs);
+    switch (a.K) {
+        case 1: hipLaunchKernelGGL(k_combine<1>, grid, block, 0, s, a); break;
+        case 2: hipLaunchKernelGGL(k_combine<2>, grid, block, 0, s, a); break;
+        case 3: hipLaunchKernelGGL(k_combine<3>, grid, block, 0, s, a); break;
+        case 4: hipLaunchKernelGGL(k_combine<4>, grid, block, 0, s, a); break;
+        case 5: hipLaunchKernelGGL(k_combine<5>, grid, block, 0, s, a); break;
+        case 6: hipLaunchKernelGGL(k_combine<6>, grid, block, 0, s, a); break;
+        case 7: hipLaunchKernelGGL(k_combine<7>, grid, block, 0, s, a); break;
+        case 8: hipLaunchKernelGGL(k_combine<8>, grid, block, 0, s, a); break;
+        case 9: hipLaunchKernelGGL(k_combine<9>, grid, block, 0, s, a); break;
+        case 10: hipLaunchKernelGGL(k_combine<10>, grid, block, 0, s, a); break;
+        case 11: hipLaunchKernelGGL(k_combine<11>, grid, block, 0, s, a); break;
+        case 12: hipLaunchKernelGGL(k_combine<12>, grid, block, 0, s, a); break;
+        case 13: hipLaunchKernelGGL(k_combine<13>, grid, block, 0, s, a); break;
+        case 14: hipLaunchKernelGGL(k_combine<14>, grid, block, 0, s, a); break;
+        case 15: hipLaunchKernelGGL(k_combine<15>, grid, block, 0, s, a); break;
+        case 16: hipLaunchKernelGGL(k_combine<16>, grid, block, 0, s, a); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,157 @@
+// Dispatch kernels: scatter each token's hidden row into the receive rows its
+// K routed entries were given by the layout.
+//
+// Dispatch carries activations to the experts (delect.ru glossary "Expert
+// parallelism (EP)", MOELayer.forward fact), written straight into the final
+// expert-grouped row (MoonEP article, section 2, zero copy), in FP8 to halve
+// the bytes (DeepEP analysis, feature list: native FP8 dispatch; both
+// benchmark set-ups: FP8 dispatch, BF16 combine).
+//
+// Each token row is read from HBM once and written K times.  A workgroup owns
+// one token and a slice of its row; its K row indices are wave-uniform and
+// live in scalar registers.  Every lane moves 16 bytes per load/store, so each
+// wave touches 1 KiB contiguous per instruction.
+//
+// FP8: a lane holds 16 channels (two 16-byte loads); the 8 lanes of one
+// 128-channel block reduce |x| with cross-lane swaps, divide amax by 448
+// (correctly rounded fp32 division), divide each value by that scale
+// (correctly rounded) and convert with the gfx950 OCP E4M3 instruction
+// (round to nearest even).  16 codes make one 16-byte store per row copy.
+#include "moe_kernels.h"
+
+namespace moe {
+namespace {
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// threads per workgroup for a row of `nvec` 16-byte vectors
+inline int row_block(int nvec) {
+    if (nvec % 256 == 0) return 256;
+    if (nvec % 128 == 0) return 128;
+    if (nvec >= 256) return 256;
+    return ((nvec + 63) / 64) * 64;
+}
+
+template <int K>
+__global__ __launch_bounds__(256) void k_dispatch_bf16(DispatchArgs a) {
+    const int t = blockIdx.x;
+    const int nvec = a.H / 8;
+    const int v = blockIdx.y * blockDim.x + threadIdx.x;
+    const u32x4 *__restrict__ hid = static_cast<const u32x4 *>(a.hidden) + static_cast<size_t>(t) * nvec;
+    u32x4 *__restrict__ recv = static_cast<u32x4 *>(a.recv);
+    const int32_t *__restrict__ pos = a.pos + static_cast<size_t>(t) * K;
+    if (v < nvec) {
+        const u32x4 x = __builtin_nontemporal_load(hid + v);
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+            const int p = pos[k];
+            if (p >= 0) __builtin_nontemporal_store(x, recv + static_cast<size_t>(p) * nvec + v);
+        }
+    }
+    if (a.recv_w != nullptr && a.topk_w != nullptr && blockIdx.y == 0 && threadIdx.x < K) {
+        const int p = pos[threadIdx.x];
+        if (p >= 0) a.recv_w[p] = a.topk_w[static_cast<size_t>(t) * K + threadIdx.x];
+    }
+}
+
+__device__ __forceinline__ float bf16_lo(unsigned int w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(unsigned int w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+template <int K>
+__global__ __launch_bounds__(256) void k_dispatch_fp8(DispatchArgs a) {
+    const int t = blockIdx.x;
+    const int n16 = a.H / 16;                       // 16-channel groups per row
+    const int g = blockIdx.y * blockDim.x + threadIdx.x;
+    const bool active = g < n16;
+    const u32x4 *__restrict__ hid = static_cast<const u32x4 *>(a.hidden) + static_cast<size_t>(t) * (a.H / 8);
+    const int32_t *__restrict__ pos = a.pos + static_cast<size_t>(t) * K;
+
+    u32x4 lo = {0u, 0u, 0u, 0u}, hi = {0u, 0u, 0u, 0u};
+    if (active) {
+        lo = __builtin_nontemporal_load(hid + 2 * g);
+        hi = __builtin_nontemporal_load(hid + 2 * g + 1);
+    }
+    float f[16];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        f[2 * i] = bf16_lo(lo[i]);
+        f[2 * i + 1] = bf16_hi(lo[i]);
+        f[8 + 2 * i] = bf16_lo(hi[i]);
+        f[8 + 2 * i + 1] = bf16_hi(hi[i]);
+    }
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(f[i]));
+    // the 8 lanes of one 128-channel block share their maximum
+    amax = fmaxf(amax, __shfl_xor(amax, 1, kWave));
+    amax = fmaxf(amax, __shfl_xor(amax, 2, kWave));
+    amax = fmaxf(amax, __shfl_xor(amax, 4, kWave));
+    const float scale = amax / 448.0f;
+
+    u32x4 q = {0u, 0u, 0u, 0u};
+    if (amax != 0.0f) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            int w = __builtin_amdgcn_cvt_pk_fp8_f32(f[4 * i] / scale, f[4 * i + 1] / scale, 0, false);
+            w = __builtin_amdgcn_cvt_pk_fp8_f32(f[4 * i + 2] / scale, f[4 * i + 3] / scale, w, true);
+            q[i] = static_cast<unsigned int>(w);
+        }
+    }
+    const int nsc = a.H / 128;
+    u32x4 *__restrict__ recv = static_cast<u32x4 *>(a.recv);
+    if (active) {
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+            const int p = pos[k];
+            if (p >= 0) {
+                __builtin_nontemporal_store(q, recv + static_cast<size_t>(p) * n16 + g);
+                if ((threadIdx.x & 7) == 0) a.recv_scales[static_cast<size_t>(p) * nsc + g / 8] = scale;
+            }
+        }
+    }
+    if (a.recv_w != nullptr && a.topk_w != nullptr && blockIdx.y == 0 && threadIdx.x < K) {
+        const int p = pos[threadIdx.x];
+        if (p >= 0) a.recv_w[p] = a.topk_w[static_cast<size_t>(t) * K + threadIdx.x];
+    }
+}
+
+#define MOE_DISPATCH_CASES(KERNEL)                                                           \
+    switch (a.K) {                                                                           \
+        case 1: hipLaunchKernelGGL(KERNEL<1>, grid, block, 0, s, a); break;                  \
+        case 2: hipLaunchKernelGGL(KERNEL<2>, grid, block, 0, s, a); break;                  \
+        case 3: hipLaunchKernelGGL(KERNEL<3>, grid, block, 0, s, a); break;                  \
+        case 4: hipLaunchKernelGGL(KERNEL<4>, grid, block, 0, s, a); break;                  \
+        case 5: hipLaunchKernelGGL(KERNEL<5>, grid, block, 0, s, a); break;                  \
+        case 6: hipLaunchKernelGGL(KERNEL<6>, grid, block, 0, s, a); break;                  \
+        case 7: hipLaunchKernelGGL(KERNEL<7>, grid, block, 0, s, a); break;                  \
+        case 8: hipLaunchKernelGGL(KERNEL<8>, grid, block, 0, s, a); break;                  \
+        case 9: hipLaunchKernelGGL(KERNEL<9>, grid, block, 0, s, a); break;                  \
+        case 10: hipLaunchKernelGGL(KERNEL<10>, grid, block, 0, s, a); break;                \
+        case 11: hipLaunchKernelGGL(KERNEL<11>, grid, block, 0, s, a); break;                \
+        case 12: hipLaunchKernelGGL(KERNEL<12>, grid, block, 0, s, a); break;                \
+        case 13: hipLaunchKernelGGL(KERNEL<13>, grid, block, 0, s, a); break;                \
+        case 14: hipLaunchKernelGGL(KERNEL<14>, grid, block, 0, s, a); break;                \
+        case 15: hipLaunchKernelGGL(KERNEL<15>, grid, block, 0, s, a); break;                \
+        case 16: hipLaunchKernelGGL(KERNEL<16>, grid, block, 0, s, a); break;                \
+        default: return hipErrorInvalidValue;                                                \
+    }
+
+}  // namespace
+
+hipError_t launch_dispatch_bf16(const DispatchArgs &a, hipStream_t s) {
+    const int nvec = a.H / 8;
+    const int bs = row_block(nvec);
+    const dim3 grid(a.S, (nvec + bs - 1) / bs), block(bs);
+    MOE_DISPATCH_CASES(k_dispatch_bf16)
+    return hipGetLastError();
+}
+
+hipError_t launch_dispatch_fp8(const DispatchArgs &a, hipStream_t s) {
+    const int n16 = a.H / 16;
+    const int bs = row_block(n16);
+    const dim3 grid(a.S, (n16 + bs - 1) / bs), block(bs);
+    MOE_DISPATCH_CASES(k_dispatch_fp8)
+    return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,263 @@
+// Layout kernels: expert histogram, padded segment scan and stable positions.
+//
+// The receive buffer is grouped by expert, experts in ascending id, so rank r's
+// partition is the contiguous run of its E/R experts (delect.ru glossary
+// "Expert parallelism (EP)": experts spread over the ranks of a group, E/R
+// local experts each; MoonEP article, section 3, Fig. 3: every rank's local
+// experts in order).  Inside an expert's segment, entries keep ascending
+// t*K+k order, so the layout is unique and reproducible.  Segments may be
+// padded to a multiple or a fixed capacity (MoonEP basic usage,
+// token_padding; search-results page, dynamic-routing snippet: zero-padding).
+//
+// Stable ranks without atomics on the order: each wave walks a contiguous run
+// of entries 64 at a time; lanes holding the same expert id find each other
+// with one ballot per key bit, take their rank from the lanes below them
+// (mbcnt), and the lowest such lane advances that wave's private LDS counter.
+// A column scan over the 16 per-wave counters then orders the waves.  Nothing
+// depends on the order in which waves or workgroups run.
+//
+// Two variants:
+//   fused  (S*K <= 16384): one 1024-thread workgroup does everything in one
+//          launch (decode-sized batches).
+//   multi  : k_layout_local ranks 4096-entry tiles per workgroup and writes a
+//          per-tile histogram; k_layout_scan (one workgroup) scans tiles and
+//          experts; k_layout_final turns tile ranks into rows.
+#include "moe_kernels.h"
+
+namespace moe {
+namespace {
+
+// Ranks J*64 consecutive entries from `base` for this wave.  s_wcnt is the
+// wave's [E] counter row (zero on entry; the wave's per-expert totals on exit).
+// key[j] = expert id or -1 (absent / out of range); local[j] = number of this
+// wave's earlier entries with the same expert.
+template <int J>
+__device__ __forceinline__ void wave_rank(const int32_t *__restrict__ idx, int N, int E, int nbits,
+                                          int base, unsigned short *s_wcnt, int (&key)[J],
+                                          int (&local)[J], int &flags) {
+    const int lane = threadIdx.x & (kWave - 1);
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+        const int i = base + j * kWave + lane;
+        const bool in = i < N;
+        const int e = in ? idx[i] : 0;
+        const bool ok = in && e >= 0 && e < E;
+        if (in && !ok) flags |= FLAG_BAD_EXPERT;
+        const uint64_t m = match_key(e, ok, nbits);
+        const int r = lanes_below(m);
+        const int before = ok ? static_cast<int>(s_wcnt[e]) : 0;
+        // every lane of the group has read the counter; the lowest one advances it
+        if (ok && r == 0) s_wcnt[e] = static_cast<unsigned short>(before + __popcll(m));
+        key[j] = ok ? e : -1;
+        local[j] = before + r;
+    }
+}
+
+// Per-wave counters of expert e -> exclusive prefixes over waves; returns the
+// workgroup's total for e.
+__device__ __forceinline__ int column_scan(unsigned short *s_cnt, int E, int e) {
+    int run = 0;
+#pragma unroll
+    for (int w = 0; w < kLayoutWaves; ++w) {
+        const int c = s_cnt[w * E + e];
+        s_cnt[w * E + e] = static_cast<unsigned short>(run);
+        run += c;
+    }
+    return run;
+}
+
+// From per-expert counts (thread e < E holds count e): placed rows, padded
+// segment lengths, their exclusive scans, and every output that depends only
+// on counts.  Also marks padding rows and the unused tail with src = -1.
+// Called by all 1024 threads; returns this thread's capacity flag.
+__device__ int finish_counts(const LayoutArgs &a, int cnt, int *s_off, int *s_pex, int2 *s_tmp) {
+    const int tid = threadIdx.x;
+    const bool is_e = tid < a.E;
+    int placed = is_e ? cnt : 0, seg = placed, flags = 0;
+    if (is_e) {
+        if (a.pad_mode == PAD_MULTIPLE) {
+            seg = (cnt + a.pad_rows - 1) / a.pad_rows * a.pad_rows;
+        } else if (a.pad_mode == PAD_CAPACITY) {
+            seg = a.pad_rows;
+            if (cnt > a.pad_rows) { placed = a.pad_rows; flags = FLAG_CAPACITY; }
+        }
+    }
+    int2 total;
+    const int2 ex = block_exclusive_scan2(make_int2(seg, placed), s_tmp, total);
+    if (is_e) {
+        s_off[tid] = ex.x;
+        s_pex[tid] = ex.y;
+        a.tpe[tid] = placed;
+        a.eoff[tid] = ex.x;
+    }
+    if (tid == 0) {
+        s_off[a.E] = total.x;
+        s_pex[a.E] = total.y;
+        a.eoff[a.E] = total.x;
+    }
+    __syncthreads();
+    const int epr = a.E / a.R;
+    if (tid < a.R) {
+        a.roff[tid] = s_off[tid * epr];
+        a.tpr[tid] = s_pex[(tid + 1) * epr] - s_pex[tid * epr];
+    }
+    if (tid == 0) a.roff[a.R] = s_off[a.E];
+    const int wave = tid / kWave, lane = tid & (kWave - 1);
+    for (int e = wave; e < a.E; e += kLayoutWaves) {
+        const int beg = s_off[e] + (s_pex[e + 1] - s_pex[e]);
+        const int end = s_off[e + 1];
+        for (int r = beg + lane; r < end; r += kWave) a.src[r] = -1;
+    }
+    for (int r = s_off[a.E] + tid; r < a.max_recv; r += kLayoutThreads) a.src[r] = -1;
+    return flags;
+}
+
+template <int J>
+__global__ __launch_bounds__(kLayoutThreads) void k_layout_fused(LayoutArgs a) {
+    extern __shared__ unsigned short s_cnt[];  // [kLayoutWaves][E]
+    __shared__ int s_off[kMaxE + 1], s_pex[kMaxE + 1];
+    __shared__ int2 s_tmp[kLayoutWaves];
+    __shared__ int s_flags;
+    const int tid = threadIdx.x, wave = tid / kWave, lane = tid & (kWave - 1);
+    for (int x = tid; x < kLayoutWaves * a.E; x += kLayoutThreads) s_cnt[x] = 0;
+    if (tid == 0) s_flags = 0;
+    __syncthreads();
+
+    int key[J], local[J], flags = 0;
+    const int base = wave * kWave * J;
+    wave_rank<J>(a.idx, a.N, a.E, a.nbits, base, s_cnt + wave * a.E, key, local, flags);
+    __syncthreads();
+    const int cnt = tid < a.E ? column_scan(s_cnt, a.E, tid) : 0;
+    flags |= finish_counts(a, cnt, s_off, s_pex, s_tmp);  // synchronises the workgroup
+
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+        const int i = base + j * kWave + lane;
+        if (i >= a.N) continue;
+        int p = -1;
+        const int e = key[j];
+        if (e >= 0) {
+            const int within = s_cnt[wave * a.E + e] + local[j];
+            if (!(a.pad_mode == PAD_CAPACITY && within >= a.pad_rows)) p = s_off[e] + within;
+        }
+        a.pos[i] = p;
+        if (p >= 0) a.src[p] = i;
+    }
+    if (flags) atomicOr(&s_flags, flags);
+    __syncthreads();
+    if (tid == 0) a.status[0] = s_flags;
+}
+
+template <int J>
+__global__ __launch_bounds__(kLayoutThreads) void k_layout_local(LayoutArgs a) {
+    extern __shared__ unsigned short s_cnt[];  // [kLayoutWaves][E]
+    __shared__ int s_flags;
+    const int tid = threadIdx.x, wave = tid / kWave, lane = tid & (kWave - 1);
+    for (int x = tid; x < kLayoutWaves * a.E; x += kLayoutThreads) s_cnt[x] = 0;
+    if (tid == 0) s_flags = 0;
+    __syncthreads();
+
+    int key[J], local[J], flags = 0;
+    const int base = blockIdx.x * kLayoutThreads * J + wave * kWave * J;
+    wave_rank<J>(a.idx, a.N, a.E, a.nbits, base, s_cnt + wave * a.E, key, local, flags);
+    if (flags) atomicOr(&s_flags, flags);
+    __syncthreads();
+    if (tid < a.E) a.blk_hist[static_cast<size_t>(blockIdx.x) * a.E + tid] = column_scan(s_cnt, a.E, tid);
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+        const int i = base + j * kWave + lane;
+        if (i < a.N) a.pos[i] = key[j] >= 0 ? s_cnt[wave * a.E + key[j]] + local[j] : -1;
+    }
+    if (tid == 0) a.blk_flags[blockIdx.x] = s_flags;
+}
+
+__global__ __launch_bounds__(kLayoutThreads) void k_layout_scan(LayoutArgs a) {
+    __shared__ int s_off[kMaxE + 1], s_pex[kMaxE + 1];
+    __shared__ int2 s_tmp[kLayoutWaves];
+    __shared__ int s_flags;
+    const int tid = threadIdx.x;
+    if (tid == 0) s_flags = 0;
+    int cnt = 0;
+    if (tid < a.E) {
+        // tile histograms -> exclusive prefixes over tiles, in tile order
+        int run = 0, b = 0;
+        for (; b + 8 <= a.nblk; b += 8) {
+            int c[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) c[u] = a.blk_hist[static_cast<size_t>(b + u) * a.E + tid];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                a.blk_hist[static_cast<size_t>(b + u) * a.E + tid] = run;
+                run += c[u];
+            }
+        }
+        for (; b < a.nblk; ++b) {
+            const int c = a.blk_hist[static_cast<size_t>(b) * a.E + tid];
+            a.blk_hist[static_cast<size_t>(b) * a.E + tid] = run;
+            run += c;
+        }
+        cnt = run;
+    }
+    int flags = 0;
+    for (int b = tid; b < a.nblk; b += kLayoutThreads) flags |= a.blk_flags[b];
+    __syncthreads();
+    flags |= finish_counts(a, cnt, s_off, s_pex, s_tmp);
+    if (flags) atomicOr(&s_flags, flags);
+    __syncthreads();
+    if (tid == 0) a.status[0] = s_flags;
+}
+
+__global__ __launch_bounds__(256) void k_layout_final(LayoutArgs a) {
+    const int stride = gridDim.x * blockDim.x;
+    for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < a.N; i += stride) {
+        const int e = a.idx[i];
+        if (e < 0 || e >= a.E) continue;  // already -1
+        const int within = a.blk_hist[static_cast<size_t>(i / kMultiTile) * a.E + e] + a.pos[i];
+        int p = -1;
+        if (!(a.pad_mode == PAD_CAPACITY && within >= a.pad_rows)) p = a.eoff[e] + within;
+        a.pos[i] = p;
+        if (p >= 0) a.src[p] = i;
+    }
+}
+
+template <int J>
+hipError_t launch_fused(const LayoutArgs &a, size_t lds, hipStream_t s) {
+    hipLaunchKernelGGL(k_layout_fused<J>, dim3(1), dim3(kLayoutThreads), lds, s, a);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+size_t layout_workspace_bytes(int64_t N, int E) {
+    if (N <= static_cast<int64_t>(kLayoutThreads) * kFusedMaxJ) return 0;
+    const int64_t nblk = (N + kMultiTile - 1) / kMultiTile;
+    const size_t bytes = static_cast<size_t>(nblk) * E * sizeof(int32_t) + static_cast<size_t>(nblk) * sizeof(int32_t);
+    return (bytes + 255) / 256 * 256;
+}
+
+hipError_t launch_layout(const LayoutArgs &a_in, hipStream_t s) {
+    LayoutArgs a = a_in;
+    const size_t lds = static_cast<size_t>(kLayoutWaves) * a.E * sizeof(unsigned short);
+    if (a.N <= kLayoutThreads * kFusedMaxJ) {
+        const int per_lane = (a.N + kLayoutThreads - 1) / kLayoutThreads;
+        if (per_lane <= 1) return launch_fused<1>(a, lds, s);
+        if (per_lane <= 2) return launch_fused<2>(a, lds, s);
+        if (per_lane <= 4) return launch_fused<4>(a, lds, s);
+        if (per_lane <= 8) return launch_fused<8>(a, lds, s);
+        return launch_fused<16>(a, lds, s);
+    }
+    a.nblk = (a.N + kMultiTile - 1) / kMultiTile;
+    a.blk_flags = a.blk_hist + static_cast<size_t>(a.nblk) * a.E;
+    hipLaunchKernelGGL(k_layout_local<kMultiJ>, dim3(a.nblk), dim3(kLayoutThreads), lds, s, a);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    hipLaunchKernelGGL(k_layout_scan, dim3(1), dim3(kLayoutThreads), 0, s, a);
+    err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    const int blocks = static_cast<int>((static_cast<int64_t>(a.N) + 255) / 256 < 2048 ? (a.N + 255) / 256 : 2048);
+    hipLaunchKernelGGL(k_layout_final, dim3(blocks), dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+}  // namespace moe

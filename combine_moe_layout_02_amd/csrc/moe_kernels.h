@@ -1,0 +1,114 @@
+// Internal declarations shared by the kernel files and the C-ABI front end.
+// Device helpers for wave64 (CDNA4): ballot-based key matching and block scans.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+constexpr int kWave = 64;
+constexpr int kLayoutThreads = 1024;              // 16 waves per layout workgroup
+constexpr int kLayoutWaves = kLayoutThreads / kWave;
+constexpr int kFusedMaxJ = 16;                    // single-workgroup layout: N <= 1024*16
+constexpr int kMultiJ = 4;                        // multi-workgroup layout tile: 4096 entries
+constexpr int kMultiTile = kLayoutThreads * kMultiJ;
+constexpr int kMaxE = 1024;
+constexpr int kMaxK = 16;
+
+enum { PAD_NONE = 0, PAD_MULTIPLE = 1, PAD_CAPACITY = 2 };
+enum { FLAG_BAD_EXPERT = 1, FLAG_CAPACITY = 2 };
+
+struct LayoutArgs {
+    const int32_t *idx;   // [N] expert ids, N = S*K
+    int32_t N, E, R, pad_mode, pad_rows, nbits;
+    int32_t max_recv;
+    int32_t *tpe, *tpr, *eoff, *roff, *pos, *src, *status;
+    int32_t *blk_hist;    // [nblk][E] (multi-workgroup path)
+    int32_t *blk_flags;   // [nblk]
+    int32_t nblk;
+};
+
+struct DispatchArgs {
+    const void *hidden;   // [S,H] bf16
+    int32_t S, H, K;
+    const int32_t *pos;   // [S,K]
+    const float *topk_w;  // [S,K] or null
+    void *recv;           // [max_recv,H] bf16 or e4m3
+    float *recv_scales;   // [max_recv,H/128] (fp8)
+    float *recv_w;        // [max_recv] or null
+};
+
+struct CombineArgs {
+    const void *y;        // [max_recv,H] bf16 expert outputs
+    int32_t S, H, K;
+    const int32_t *pos;   // [S,K]
+    const float *w;       // [S,K] or null (weight 1)
+    const void *shared;   // [S,H] bf16 or null
+    void *out;            // [S,H] bf16
+};
+
+size_t layout_workspace_bytes(int64_t N, int E);
+hipError_t launch_layout(const LayoutArgs &a, hipStream_t stream);
+hipError_t launch_dispatch_bf16(const DispatchArgs &a, hipStream_t stream);
+hipError_t launch_dispatch_fp8(const DispatchArgs &a, hipStream_t stream);
+hipError_t launch_combine(const CombineArgs &a, hipStream_t stream);
+
+// ---------------------------------------------------------------------------
+// device helpers
+// ---------------------------------------------------------------------------
+
+// Number of set bits of `m` below this lane (v_mbcnt_lo / v_mbcnt_hi).
+__device__ __forceinline__ int lanes_below(uint64_t m) {
+    return __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(m >> 32),
+                                     __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0u));
+}
+
+// Mask of the active lanes holding the same key as this lane: one ballot per
+// key bit (nbits of them), intersecting "same bit" sets.  Must be called by
+// the whole wave in uniform control flow; lanes with active == false take part
+// in the ballots but belong to no mask.
+__device__ __forceinline__ uint64_t match_key(int key, bool active, int nbits) {
+    uint64_t m = __ballot(active);
+    for (int b = 0; b < nbits; ++b) {
+        const bool bit = (key >> b) & 1;
+        const uint64_t bb = __ballot(bit);
+        m &= bit ? bb : ~bb;
+    }
+    return m;
+}
+
+// Inclusive prefix sum of an int pair across the 64 lanes of a wave.
+__device__ __forceinline__ int2 wave_inclusive_scan2(int2 v) {
+    const int lane = threadIdx.x & (kWave - 1);
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+        const int ax = __shfl_up(v.x, d, kWave);
+        const int ay = __shfl_up(v.y, d, kWave);
+        if (lane >= d) { v.x += ax; v.y += ay; }
+    }
+    return v;
+}
+
+// Exclusive prefix sum of an int pair across a 1024-thread workgroup, in
+// thread order.  `s_tmp` holds kLayoutWaves entries.  Returns the prefix and
+// the workgroup total.  Contains __syncthreads: call from every thread.
+__device__ __forceinline__ int2 block_exclusive_scan2(int2 v, int2 *s_tmp, int2 &total) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
+    const int2 inc = wave_inclusive_scan2(v);
+    if (lane == kWave - 1) s_tmp[wave] = inc;
+    __syncthreads();
+    int2 before = make_int2(0, 0), all = make_int2(0, 0);
+#pragma unroll
+    for (int w = 0; w < kLayoutWaves; ++w) {
+        const int2 t = s_tmp[w];
+        if (w < wave) { before.x += t.x; before.y += t.y; }
+        all.x += t.x; all.y += t.y;
+    }
+    __syncthreads();
+    total = all;
+    return make_int2(before.x + inc.x - v.x, before.y + inc.y - v.y);
+}
+
+}  // namespace moe

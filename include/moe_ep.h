@@ -1,0 +1,169 @@
+/*
+ * moe_ep.h -- C ABI of the MI355X (gfx950) MoE expert-parallel layout,
+ * dispatch and combine library (libmoe_ep.so).
+ *
+ * The three calls are the data-parallel hot path of expert parallelism:
+ *
+ *   moe_layout    top-k routing -> per-expert / per-rank counts, padded segment
+ *                 offsets, and the maps between (token, k) entries and rows of
+ *                 the receive buffer.
+ *   moe_dispatch  token rows -> rows of the expert-grouped, rank-partitioned
+ *                 receive buffer, bit-copied bf16 or FP8 E4M3 with one fp32
+ *                 scale per 128 channels.
+ *   moe_combine   expert output rows -> token order, as the route-weighted sum
+ *                 of each token's K rows (fp32 accumulation), plus an optional
+ *                 shared-expert output.
+ *
+ * What the operations are (passages):
+ *   - Experts of a layer are spread over the ranks of an EP group; E must
+ *     divide by the group size R and each rank holds E/R local experts
+ *     (delect.ru glossary "Expert parallelism (EP)", confirmed facts: the
+ *     DeepSpeed v0.14.5 example, 8 experts on 4 ranks).  Rank r owns experts
+ *     [r*E/R, (r+1)*E/R) (MoonEP article, section 3 and Fig. 3: rows [0,E) of
+ *     the weight buffer hold every rank's local experts in order).
+ *   - Activations travel to the experts and the results travel back and are
+ *     merged (same glossary, the MOELayer.forward fact); the all-to-all pair
+ *     is called dispatch and combine (DeepEP analysis, "DeepEP introduction").
+ *   - Dispatch sends FP8, combine returns BF16 (DeepEP analysis, feature list
+ *     and the set-up of both benchmark tables).
+ *   - Each token is written straight into its final expert-grouped row on the
+ *     receiving rank; static shapes avoid any per-layer host sync (MoonEP
+ *     article, section 2, "zero copy" and static layout).  Per-expert padding
+ *     to a static shape (search-results page, the dynamic-routing snippet:
+ *     drop tokens or zero-pad; MoonEP basic usage, token_padding=128).
+ *
+ * The R ranks of one EP group are simulated on one GPU as rank-major
+ * partitions of one receive buffer: partition r is exactly what GPU r would
+ * receive.
+ *
+ * Conventions for every call:
+ *   - All array arguments are DEVICE pointers, row-major and contiguous, owned
+ *     by the caller; the library never allocates, frees or keeps them.
+ *     Descriptor structs are HOST pointers read during the call only.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and
+ *     runs asynchronously; no call copies device -> host or synchronises.
+ *   - Argument errors are returned synchronously, before anything is
+ *     enqueued.  Data errors (an expert id outside [0,E), a capacity
+ *     overflow) are found on the device and written to layout->status[0].
+ *   - The library holds no global state: calls are reentrant and thread safe.
+ *     Calls on one stream run in order; calls on different streams that share
+ *     output buffers race.
+ *   - Limits: 0 <= S, 1 <= K <= 16, 1 <= E <= 1024, R divides E,
+ *     S*K and every row count below 2^31.
+ */
+#ifndef MOE_EP_H
+#define MOE_EP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MOE_OK = 0,
+    MOE_ERR_NULL = 1,      /* a required pointer is NULL */
+    MOE_ERR_SHAPE = 2,     /* a size or mode is outside the limits above */
+    MOE_ERR_ALIGN = 3,     /* a row buffer is not 16-byte aligned */
+    MOE_ERR_WORKSPACE = 4, /* workspace missing or smaller than required */
+    MOE_ERR_HIP = 5        /* the HIP runtime refused a launch */
+} moe_status;
+
+/* How each expert's segment of the receive buffer is sized. */
+typedef enum {
+    MOE_PAD_NONE = 0,      /* exactly the expert's entries */
+    MOE_PAD_MULTIPLE = 1,  /* rounded up to a multiple of pad_rows (0 stays 0) */
+    MOE_PAD_CAPACITY = 2   /* exactly pad_rows; entries beyond are not placed */
+} moe_pad_mode;
+
+/* Bits of layout->status[0]. */
+enum {
+    MOE_FLAG_BAD_EXPERT = 1, /* some topk_idx outside [0,E); that entry got pos = -1 */
+    MOE_FLAG_CAPACITY = 2    /* some expert had more than pad_rows entries (CAPACITY);
+                                the entries past the capacity got pos = -1 */
+};
+
+/* Shape of one batch (host struct). */
+typedef struct {
+    int32_t S;        /* tokens */
+    int32_t K;        /* experts per token */
+    int32_t E;        /* experts */
+    int32_t R;        /* EP ranks; rank r owns experts [r*E/R, (r+1)*E/R) */
+    int32_t pad_mode; /* moe_pad_mode */
+    int32_t pad_rows; /* multiple or capacity; ignored for MOE_PAD_NONE */
+} moe_layout_desc;
+
+/* The layout of one batch: outputs of moe_layout, inputs of dispatch and
+ * combine (host struct holding device pointers, all int32). */
+typedef struct {
+    int32_t *tokens_per_expert; /* [E]   rows placed in each expert's segment */
+    int32_t *tokens_per_rank;   /* [R]   rows placed in each rank's partition */
+    int32_t *expert_offset;     /* [E+1] first row of each expert's segment; [E] = rows used */
+    int32_t *rank_offset;       /* [R+1] first row of each rank's partition */
+    int32_t *pos;               /* [S*K] row of entry (t,k) at t*K+k, or -1 */
+    int32_t *src;               /* [moe_max_recv_rows] entry t*K+k held by each row, -1 if none */
+    int32_t *status;            /* [1]   MOE_FLAG_* of this batch (overwritten) */
+} moe_layout_bufs;
+
+/* Rows the receive buffer (and src) must hold for ANY routing of this shape:
+ * S*K (NONE), S*K + E*(pad_rows-1) (MULTIPLE), E*pad_rows (CAPACITY).
+ * Host only.  Returns -1 if the shape is invalid. */
+int64_t moe_max_recv_rows(const moe_layout_desc *desc);
+
+/* Device workspace bytes moe_layout needs for this shape (0 for small
+ * batches).  Host only.  Returns 0 for an invalid shape too; moe_layout then
+ * reports MOE_ERR_SHAPE. */
+size_t moe_layout_workspace_bytes(const moe_layout_desc *desc);
+
+/* Layout of one batch from its top-k routing.
+ *   topk_idx  [S,K] int32 device: expert of entry (t,k).
+ *   out       every pointer required; src has moe_max_recv_rows entries.
+ *   workspace device scratch of at least moe_layout_workspace_bytes (may be
+ *             NULL when that is 0); 16-byte aligned; contents need no init.
+ * Inside each expert's segment, rows follow ascending t*K+k (stable); ranks
+ * and experts appear in ascending order (rank-major).  Padding rows are not
+ * touched in the row buffers; their src is -1. */
+moe_status moe_layout(const moe_layout_desc *desc, const int32_t *topk_idx,
+                      const moe_layout_bufs *out, void *workspace, size_t workspace_bytes,
+                      void *stream);
+
+/* Dispatch: row pos[t,k] of the receive buffer gets token t's hidden row.
+ *   hidden      [S,H] bf16 device, 16-byte aligned, H % 8 == 0.
+ *   topk_idx    [S,K] int32; the expert ids already folded into `layout`
+ *               (kept for the calling convention; may be NULL).
+ *   topk_w      [S,K] fp32 or NULL; with recv_w, recv_w[pos[t,k]] = topk_w[t,k].
+ *   fp8 == 0    recv [max_recv,H] bf16 gets the row bit for bit.
+ *   fp8 != 0    H % 128 == 0; recv [max_recv,H] E4M3FN bytes and recv_scales
+ *               [max_recv,H/128] fp32: per 128-channel block b of token t,
+ *               scale = amax/448 (fp32 division, amax = max |x|) and
+ *               code = E4M3FN(x/scale) (fp32 division, round to nearest even,
+ *               saturating at +-448); an all-zero block has scale 0 and codes 0.
+ *   recv_w      [max_recv] fp32 or NULL.
+ * Rows that no entry maps to (padding, unused tail) are not written. */
+moe_status moe_dispatch(const moe_layout_desc *desc, const moe_layout_bufs *layout,
+                        const void *hidden, int32_t H, const int32_t *topk_idx,
+                        const float *topk_w, int32_t fp8, void *recv, float *recv_scales,
+                        float *recv_w, void *stream);
+
+/* Combine: out[t,c] = bf16_rne( (fma chain over k = 0..K-1 of
+ *                                w[t,k] * expert_out[pos[t,k], c], from +0.0)
+ *                               + shared_out[t,c] ).
+ *   expert_out  [max_recv,H] bf16 device, 16-byte aligned, H % 8 == 0; only rows
+ *               some pos[t,k] points to are read.
+ *   w           [S,K] fp32 in token order, or NULL for weight 1.
+ *   shared_out  [S,H] bf16 or NULL (then nothing is added).
+ *   out         [S,H] bf16, 16-byte aligned.
+ * Entries with pos = -1 are skipped. */
+moe_status moe_combine(const moe_layout_desc *desc, const moe_layout_bufs *layout,
+                       const void *expert_out, int32_t H, const float *w,
+                       const void *shared_out, void *out, void *stream);
+
+/* Static string naming a moe_status value. */
+const char *moe_status_str(int32_t status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_EP_H */

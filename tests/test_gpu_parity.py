@@ -1,0 +1,268 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Bar: layout, maps, counts, offsets, bf16 dispatch, FP8 codes and scales are
+bit-exact; combine is within 1 bf16 ulp per element with max abs error
+<= 1e-2 * max |out|.  Every input comes from the seeded generators in
+`workloads`; every expected value from `oracle` on the same inputs.
+Padding rows of the receive buffer are pre-filled with a NaN pattern: they
+must stay untouched by dispatch and unread by combine.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from parity_helpers import (POISON_BF16, POISON_U8, assert_combine_matches, compare_layout, dev_bf16,
+                            host_bits)
+from workloads import (CONFIGS, PAD_CAPACITY, PAD_MULTIPLE, PAD_NONE, WorkloadConfig, make_workload,
+                       random_expert_out_bits)
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+@pytest.fixture(scope="module")
+def moe():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import combine_moe_layout_02_amd as m
+    return m
+
+
+def say(msg: str):
+    print(msg, flush=True)
+
+
+def run_and_check(moe, cfg: WorkloadConfig, topk_idx: np.ndarray, hidden: np.ndarray, topk_w: np.ndarray,
+                  shared=None, fp8=False, seed=1, combine_weights=True):
+    """Full path on the GPU vs the oracle.  Returns the oracle layout."""
+    S, K, E, R, H = cfg.S, cfg.K, cfg.E, cfg.R, cfg.H
+    say(f"case {cfg.name}: S={S} H={H} E={E} K={K} R={R} pad={cfg.pad_mode}/{cfg.pad_rows} fp8={fp8}")
+    desc = moe.LayoutDesc(S, K, E, R, cfg.pad_mode, cfg.pad_rows)
+    rows = moe.moe_max_recv_rows(desc)
+    ref = oracle.layout(topk_idx, E, R, cfg.pad_mode, cfg.pad_rows)
+    assert rows == len(ref.src)
+
+    idx_d = torch.from_numpy(np.ascontiguousarray(topk_idx)).to(DEV)
+    hid_d = dev_bf16(hidden, DEV)
+    w_d = torch.from_numpy(np.ascontiguousarray(topk_w)).to(DEV)
+    lay = moe.moe_layout(desc, idx_d)
+    torch.cuda.synchronize()
+    compare_layout(lay, ref, f"{cfg.name} layout")
+
+    valid = ref.src >= 0
+    if fp8:
+        recv = torch.full((rows, H), POISON_U8, dtype=torch.uint8, device=DEV)
+        scales = torch.full((rows, H // 128), float("nan"), dtype=torch.float32, device=DEV)
+        recv_w = torch.full((rows,), float("nan"), dtype=torch.float32, device=DEV)
+        moe.moe_dispatch(desc, lay, hid_d, idx_d, w_d, fp8=True, recv=recv, recv_scales=scales, recv_w=recv_w)
+        torch.cuda.synchronize()
+        rc, rs, rw = oracle.dispatch_fp8(hidden, ref.pos, rows, topk_w)
+        got_c, got_s = recv.cpu().numpy(), scales.cpu().numpy()
+        bad = np.nonzero(np.any(got_c[valid] != rc[valid], axis=1))[0]
+        assert bad.size == 0, f"fp8 codes differ in {bad.size} rows"
+        assert np.array_equal(got_s[valid].view(np.uint32), rs[valid].view(np.uint32)), "fp8 scales differ"
+        assert np.all(got_c[~valid] == POISON_U8), "dispatch wrote a padding row"
+        y_ref = oracle.dequant_identity_expert(rc, rs)
+    else:
+        recv = torch.full((rows, H), POISON_BF16, dtype=torch.int16, device=DEV).view(torch.bfloat16)
+        recv_w = torch.full((rows,), float("nan"), dtype=torch.float32, device=DEV)
+        moe.moe_dispatch(desc, lay, hid_d, idx_d, w_d, fp8=False, recv=recv, recv_w=recv_w)
+        torch.cuda.synchronize()
+        rb, rw = oracle.dispatch_bf16(hidden, ref.pos, rows, topk_w)
+        got = host_bits(recv)
+        bad = np.nonzero(np.any(got[valid] != rb[valid], axis=1))[0]
+        assert bad.size == 0, f"bf16 rows differ in {bad.size} rows"
+        assert np.all(got[~valid] == POISON_BF16), "dispatch wrote a padding row"
+        y_ref = rb
+    assert np.array_equal(recv_w.cpu().numpy()[valid].view(np.uint32), rw[valid].view(np.uint32))
+
+    w_comb = topk_w if combine_weights else None
+    wc_d = w_d if combine_weights else None
+    sh_d = dev_bf16(shared, DEV) if shared is not None else None
+    # identity experts: the oracle's own dispatch output (dequantised for FP8)
+    y = np.where(valid[:, None], y_ref, np.uint16(POISON_BF16)).astype(np.uint16)
+    out = moe.moe_combine(desc, lay, dev_bf16(y, DEV), wc_d, sh_d)
+    torch.cuda.synchronize()
+    nx = assert_combine_matches(host_bits(out), oracle.combine(y, ref.pos, w_comb, shared), "combine/identity")
+    # random expert outputs
+    y = random_expert_out_bits(seed, rows, H, row_mask=valid, poison=POISON_BF16)
+    out = moe.moe_combine(desc, lay, dev_bf16(y, DEV), wc_d, sh_d)
+    torch.cuda.synchronize()
+    nr = assert_combine_matches(host_bits(out), oracle.combine(y, ref.pos, w_comb, shared), "combine/random")
+    say(f"  ok (combine elements not bit-identical: identity {nx}, random {nr})")
+    return ref
+
+
+@pytest.mark.parametrize("name", list(CONFIGS))
+def test_config_parity(moe, name):
+    cfg = CONFIGS[name]
+    w = make_workload(cfg)
+    run_and_check(moe, cfg, w.topk_idx, w.hidden, w.topk_w, shared=w.shared, fp8=cfg.fp8, seed=w.seed)
+
+
+def _case(name, S, H, E, K, R, pad_mode=PAD_NONE, pad_rows=0, routing="uniform"):
+    return WorkloadConfig(name, S=S, H=H, E=E, K=K, R=R, pad_mode=pad_mode, pad_rows=pad_rows, routing=routing)
+
+
+EDGE = [
+    # (config, fp8, routing override, shared)
+    (_case("one-entry", 1, 8, 1, 1, 1), False, None, False),
+    (_case("ragged-row", 333, 136, 16, 16, 4), False, None, True),          # K = E, 17 vectors per row
+    (_case("E1024-fp8-mult7", 777, 256, 1024, 3, 8, PAD_MULTIPLE, 7), True, None, False),
+    (_case("multi-ragged-tail", 16385, 8, 5, 1, 5), False, None, False),    # one entry past one workgroup
+    (_case("multi-capacity-overflow", 5000, 1024, 256, 4, 8, PAD_CAPACITY, 90), False, None, False),
+    (_case("one-hot-expert", 3000, 64, 64, 1, 4, PAD_MULTIPLE, 128), False, "all5", False),
+    (_case("bad-ids-fused", 100, 128, 32, 4, 4), True, "bad", False),
+    (_case("bad-ids-multi", 6000, 64, 32, 4, 4, PAD_MULTIPLE, 3), False, "bad", True),
+    (_case("duplicates", 300, 72, 8, 6, 2, PAD_CAPACITY, 300), False, "dup", False),
+    (_case("multi-zipf", 8192, 64, 256, 8, 8, PAD_MULTIPLE, 128), False, "zipf", False),
+    (_case("multi-K16-E1024", 2048, 128, 1024, 16, 1), True, None, False),
+    (_case("pad-multiple-1", 50, 8, 4, 2, 2, PAD_MULTIPLE, 1), False, None, False),
+]
+
+
+@pytest.mark.parametrize("case", EDGE, ids=[c[0].name for c in EDGE])
+def test_edge_cases(moe, case):
+    cfg, fp8, routing, with_shared = case
+    seed = 9000 + EDGE.index(case)
+    rng = np.random.default_rng(seed)
+    if routing == "zipf":
+        import dataclasses
+        cfg = dataclasses.replace(cfg, routing="zipf", target_maxvio=20.0)
+    w = make_workload(cfg, seed=seed) if routing in (None, "zipf") else None
+    hidden = make_workload(dataclasses_replace_uniform(cfg), seed=seed).hidden if w is None else w.hidden
+    if routing == "all5":
+        idx = np.full((cfg.S, cfg.K), 5, np.int32)
+    elif routing == "bad":
+        idx = rng.integers(0, cfg.E, (cfg.S, cfg.K)).astype(np.int32)
+        hit = rng.random((cfg.S, cfg.K)) < 0.01
+        idx[hit] = rng.choice([-1, cfg.E, cfg.E + 7, -100], int(hit.sum()))
+    elif routing == "dup":
+        idx = rng.integers(0, cfg.E, (cfg.S, cfg.K)).astype(np.int32)
+    else:
+        idx = w.topk_idx
+    tw = rng.random((cfg.S, cfg.K)).astype(np.float32)
+    tw /= tw.sum(axis=1, keepdims=True)
+    shared = make_workload(dataclasses_replace_uniform(cfg), seed=seed + 1).hidden if with_shared else None
+    ref = run_and_check(moe, cfg, idx, hidden, tw, shared=shared, fp8=fp8, seed=seed)
+    if routing == "bad":
+        assert ref.status[0] & oracle.FLAG_BAD_EXPERT
+    if cfg.name == "multi-capacity-overflow":
+        assert ref.status[0] & oracle.FLAG_CAPACITY
+
+
+def dataclasses_replace_uniform(cfg):
+    import dataclasses
+    return dataclasses.replace(cfg, routing="uniform", K=min(cfg.K, cfg.E))
+
+
+def test_empty_batch(moe):
+    for pad_mode, pad_rows in ((PAD_NONE, 0), (PAD_MULTIPLE, 4), (PAD_CAPACITY, 3)):
+        say(f"case empty: pad={pad_mode}/{pad_rows}")
+        desc = moe.LayoutDesc(0, 2, 8, 2, pad_mode, pad_rows)
+        idx = torch.empty((0, 2), dtype=torch.int32, device=DEV)
+        lay = moe.alloc_layout(desc, DEV)
+        lay.status.fill_(-1)
+        moe.moe_layout(desc, idx, lay)
+        torch.cuda.synchronize()
+        compare_layout(lay, oracle.layout(np.zeros((0, 2), np.int32), 8, 2, pad_mode, pad_rows), "empty")
+        hid = torch.empty((0, 64), dtype=torch.bfloat16, device=DEV)
+        moe.moe_dispatch(desc, lay, hid)
+        y = torch.zeros((max(moe.moe_max_recv_rows(desc), 1), 64), dtype=torch.bfloat16, device=DEV)
+        out = moe.moe_combine(desc, lay, y)
+        assert out.shape == (0, 64)
+
+
+def test_fp8_converter_sweep(moe):
+    """Every finite bf16 value with |v| <= 448, in 128-channel blocks whose first
+    element is +-448 (scale exactly 1, so the quotient is the value itself):
+    the hardware E4M3 conversion against the oracle's encoder, bit for bit.
+    This covers every E4M3 rounding midpoint (they are bf16 values), ties,
+    subnormals, signed zeros and the saturation edge."""
+    b = np.arange(0x8000, dtype=np.uint32)
+    vals = (b << 16).view(np.float32)
+    keep = b[np.abs(vals) <= 448.0].astype(np.uint16)
+    allv = np.concatenate([keep, keep | np.uint16(0x8000)])
+    per = 127
+    nblk = -(-allv.size // per)
+    H = 7168
+    rows = -(-nblk // (H // 128))
+    blocks = np.zeros((rows * (H // 128), 128), np.uint16)
+    blocks[:, 0] = np.where(np.arange(blocks.shape[0]) % 2 == 0, 0x43E0, 0xC3E0)   # +448 / -448
+    body = np.zeros(blocks.shape[0] * per, np.uint16)
+    body[:allv.size] = allv
+    blocks[:, 1:] = body.reshape(-1, per)
+    hidden = blocks.reshape(rows, H)
+    cfg = _case("fp8-sweep", rows, H, 1, 1, 1)
+    idx = np.zeros((rows, 1), np.int32)
+    tw = np.ones((rows, 1), np.float32)
+    say(f"case fp8-sweep: {allv.size} bf16 values in {rows} rows")
+    desc = moe.LayoutDesc(rows, 1, 1, 1)
+    lay = moe.moe_layout(desc, torch.from_numpy(idx).to(DEV))
+    recv, scales, _ = moe.moe_dispatch(desc, lay, dev_bf16(hidden, DEV), fp8=True)
+    torch.cuda.synchronize()
+    ref = oracle.layout(idx, 1, 1)
+    rc, rs, _ = oracle.dispatch_fp8(hidden, ref.pos, rows)
+    assert np.all(rs == 1.0)
+    got = recv.cpu().numpy()
+    bad = np.nonzero(got.reshape(-1) != rc.reshape(-1))[0]
+    hv = hidden.reshape(-1)
+    assert bad.size == 0, [(hex(int(hv[i])), int(got.reshape(-1)[i]), int(rc.reshape(-1)[i])) for i in bad[:8]]
+    assert np.array_equal(scales.cpu().numpy(), rs)
+    del cfg, tw
+
+
+def test_combine_rounding_order_pins(moe):
+    """Hand-worked cases where only an fp32 fma chain in ascending k gives the
+    right bf16 bit (the same cases pin the oracle): 1+2^-8 then
+    0x1.fc07f2p-25 * (1+2^-7) -> 0x3F81; 1+2^-8, 3*2^-26, 3*2^-26 -> 0x3F80."""
+    H = 8
+    one, one_p = 0x3F80, 0x3F81
+    for ws, ys, want in (([1 + 2 ** -8, float.fromhex("0x1.fc07f2p-25")], [one, one_p], 0x3F81),
+                         ([1 + 2 ** -8, 3 * 2 ** -26, 3 * 2 ** -26], [one, one, one], 0x3F80)):
+        K = len(ws)
+        say(f"case order-pin K={K}")
+        desc = moe.LayoutDesc(1, K, K, 1)
+        idx = torch.arange(K, dtype=torch.int32, device=DEV).reshape(1, K)
+        lay = moe.moe_layout(desc, idx)
+        y = np.repeat(np.array(ys, np.uint16)[:, None], H, axis=1)
+        out = moe.moe_combine(desc, lay, dev_bf16(y, DEV), torch.tensor([ws], dtype=torch.float32, device=DEV))
+        assert host_bits(out).tolist() == [[want] * H]
+
+
+def test_round_trip_on_gpu(moe):
+    """combine(dispatch(x)) on the GPU alone, identity experts, weights summing
+    to 1: x comes back bit for bit (a -0.0 input comes back as +0.0)."""
+    cfg = CONFIGS["dsmoe16b"]
+    w = make_workload(cfg)
+    say("case round-trip dsmoe16b")
+    desc = moe.LayoutDesc(cfg.S, cfg.K, cfg.E, cfg.R)
+    lay = moe.moe_layout(desc, torch.from_numpy(w.topk_idx).to(DEV))
+    tw = torch.from_numpy(w.topk_w).to(DEV)
+    recv, _, _ = moe.moe_dispatch(desc, lay, dev_bf16(w.hidden, DEV), topk_w=tw)
+    out = moe.moe_combine(desc, lay, recv, tw)
+    want = np.where((w.hidden & 0x7FFF) == 0, 0, w.hidden)
+    assert np.array_equal(host_bits(out), want)
+
+
+def test_determinism_and_streams(moe):
+    """Two runs, one on a side stream, give identical bits."""
+    cfg = CONFIGS["prefill"]
+    w = make_workload(cfg)
+    say("case determinism prefill")
+    desc = moe.LayoutDesc(cfg.S, cfg.K, cfg.E, cfg.R)
+    idx = torch.from_numpy(w.topk_idx).to(DEV)
+    hid = dev_bf16(w.hidden, DEV)
+    torch.cuda.synchronize()
+    outs = []
+    side = torch.cuda.Stream()
+    for stream in (None, side):
+        with torch.cuda.stream(stream if stream is not None else torch.cuda.current_stream()):
+            lay = moe.moe_layout(desc, idx, stream=stream)
+            recv, sc, _ = moe.moe_dispatch(desc, lay, hid, fp8=True, stream=stream)
+        torch.cuda.synchronize()
+        outs.append((lay.pos.cpu().numpy(), lay.src.cpu().numpy(), recv.cpu().numpy(), sc.cpu().numpy()))
+    for a, b in zip(*outs):
+        assert np.array_equal(a, b)
