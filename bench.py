@@ -34,6 +34,7 @@ if ROOT not in sys.path:
 METRIC = "dispatch+combine HBM GB/s (% of peak) at S=4096,H=7168,E=256,K=8; µs at S=128"
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, 8 TB/s
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+CSRC = os.path.join(ROOT, "combine_moe_layout_02_amd", "csrc")
 
 
 # ---------------------------------------------------------------------------
@@ -70,21 +71,24 @@ def combine_bytes(S: int, K: int, H: int, placed: int, shared: bool) -> int:
 
 # ---------------------------------------------------------------------------
 
-def file_sha256(path: str) -> str:
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+def sources_sha256(names) -> str:
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(CSRC, n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
-def load_traffic(kernel_src: str, workload: str):
+def load_traffic(key: str):
     """HBM bytes per launch from the committed rocprofv3 counter runs, or None
-    when the kernel source changed since they were taken."""
+    when a source of the kernel changed since they were taken."""
     try:
         with open(TRAFFIC_FILE) as f:
             rec = json.load(f)
     except (OSError, ValueError):
         return None
-    entry = rec.get(workload)
-    if not entry or entry.get("source_sha256") != file_sha256(kernel_src):
+    entry = rec.get(key)
+    if not entry or entry.get("source_sha256") != sources_sha256(entry.get("sources", [])):
         return None
     return entry.get("bytes_per_launch")
 
@@ -141,6 +145,7 @@ class Run:
     def bytes(self):
         import torch
         if self.placed is None:
+            self.layout_call()
             torch.cuda.synchronize()
             self.placed = int(self.layout.tokens_per_expert.sum().item())
         c = self.cfg
@@ -279,9 +284,9 @@ def main(argv=None):
     dom = "combine" if cb >= db else "dispatch"
     dom_bytes, dom_ms = (cb, t["combine_ms"]) if dom == "combine" else (db, t["dispatch_ms"])
     achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
-    src = os.path.join(ROOT, "combine_moe_layout_02_amd", "csrc", f"{dom}.hip")
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": load_traffic(src, f"{dom}/{cfg.name}"),
+                "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": load_traffic(f"{dom}/{cfg.name}"),
+                "traffic_unit": "HBM bytes per launch",
                 "kernel": dom, "algorithmic_bytes_per_launch": dom_bytes,
                 "avg_launch_us": round(dom_ms * 1e3, 2)}
 

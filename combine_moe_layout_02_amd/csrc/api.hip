@@ -94,6 +94,7 @@ moe_status moe_dispatch(const moe_layout_desc *desc, const moe_layout_bufs *layo
     if (desc == nullptr || layout == nullptr) return MOE_ERR_NULL;
     if (!desc_ok(desc) || max_rows(desc) < 0 || H < 8 || H % 8 != 0) return MOE_ERR_SHAPE;
     if (fp8 && H % 128 != 0) return MOE_ERR_SHAPE;
+    if ((H / (fp8 ? 16 : 8) + moe::kWave - 1) / moe::kWave > 65535) return MOE_ERR_SHAPE;  // grid.y
     if (desc->S == 0) return MOE_OK;
     if (hidden == nullptr || recv == nullptr || layout->pos == nullptr) return MOE_ERR_NULL;
     if (fp8 && recv_scales == nullptr) return MOE_ERR_NULL;
@@ -119,6 +120,8 @@ moe_status moe_combine(const moe_layout_desc *desc, const moe_layout_bufs *layou
                        int32_t H, const float *w, const void *shared_out, void *out, void *stream) {
     if (desc == nullptr || layout == nullptr) return MOE_ERR_NULL;
     if (!desc_ok(desc) || max_rows(desc) < 0 || H < 8 || H % 8 != 0) return MOE_ERR_SHAPE;
+    // one workgroup per (token, 512-channel chunk)
+    if (static_cast<int64_t>(desc->S) * ((H / 8 + moe::kWave - 1) / moe::kWave) > INT32_MAX) return MOE_ERR_SHAPE;
     if (desc->S == 0) return MOE_OK;
     if (expert_out == nullptr || out == nullptr || layout->pos == nullptr) return MOE_ERR_NULL;
     if (!aligned(expert_out, 16) || !aligned(out, 16) || !aligned(shared_out, 16) || !aligned(w, 4) ||

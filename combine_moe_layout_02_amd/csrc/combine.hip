@@ -9,20 +9,20 @@
 //
 // out[t,c] = bf16_rne( fma-chain over k = 0..K-1 of w[t,k] * y[pos[t,k], c],
 //                      starting at +0.0, then + shared[t,c] ).
-// A lane owns 8 channels of one token: it issues all K 16-byte gathers before
-// the first fma (K loads in flight), keeps 8 fp32 accumulators, and writes one
-// 16-byte store.  The K row indices and weights are wave-uniform scalars.
+// One wavefront per 512-channel (1 KiB) chunk of a token row.  A lane owns 8
+// channels: it issues all K 16-byte gathers before the first fma (K loads in
+// flight), keeps 8 fp32 accumulators, and writes one 16-byte store.  The K row
+// indices and weights are wave-uniform scalars.  Workgroups are numbered
+// chunk-fastest, so the waves running at one time cover whole source rows
+// rather than one chunk of thousands of rows: on MI355X that DRAM-friendlier
+// order measured about 6% faster than a token-fastest order.
 #include "moe_kernels.h"
 
 namespace moe {
 namespace {
 
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-
-__device__ __forceinline__ float bf16_lo(unsigned int w) { return __uint_as_float(w << 16); }
-__device__ __forceinline__ float bf16_hi(unsigned int w) { return __uint_as_float(w & 0xFFFF0000u); }
 
 // two fp32 -> packed bf16 pair, round to nearest even (v_cvt_pk_bf16_f32)
 __device__ __forceinline__ unsigned int pack_bf16x2(float lo, float hi) {
@@ -31,18 +31,11 @@ __device__ __forceinline__ unsigned int pack_bf16x2(float lo, float hi) {
     return __builtin_bit_cast(unsigned int, b);
 }
 
-inline int row_block(int nvec) {
-    if (nvec % 256 == 0) return 256;
-    if (nvec % 128 == 0) return 128;
-    if (nvec >= 256) return 256;
-    return ((nvec + 63) / 64) * 64;
-}
-
 template <int K>
-__global__ __launch_bounds__(256) void k_combine(CombineArgs a) {
-    const int t = blockIdx.x;
+__global__ __launch_bounds__(kWave) void k_combine(CombineArgs a, int nchunk) {
+    const int t = blockIdx.x / nchunk;
     const int nvec = a.H / 8;
-    const int v = blockIdx.y * blockDim.x + threadIdx.x;
+    const int v = (blockIdx.x % nchunk) * kWave + threadIdx.x;
     if (v >= nvec) return;
     const u32x4 *__restrict__ y = static_cast<const u32x4 *>(a.y);
     const int32_t *__restrict__ pos = a.pos + static_cast<size_t>(t) * K;
@@ -83,32 +76,34 @@ __global__ __launch_bounds__(256) void k_combine(CombineArgs a) {
     u32x4 o;
 #pragma unroll
     for (int i = 0; i < 4; ++i) o[i] = pack_bf16x2(acc[2 * i], acc[2 * i + 1]);
-    __builtin_nontemporal_store(o, static_cast<u32x4 *>(a.out) + static_cast<size_t>(t) * nvec + v);
+    // ordinary store for out, non-temporal loads for the gathered rows: the
+    // faster pairing in measurements on MI355X
+    static_cast<u32x4 *>(a.out)[static_cast<size_t>(t) * nvec + v] = o;
 }
 
 }  // namespace
 
 hipError_t launch_combine(const CombineArgs &a, hipStream_t s) {
     const int nvec = a.H / 8;
-    const int bs = row_block(nvec);
-    const dim3 grid(a.S, (nvec + bs - 1) / bs), block(bs);
+    const int nchunk = (nvec + kWave - 1) / kWave;
+    const dim3 grid(static_cast<unsigned>(static_cast<int64_t>(a.S) * nchunk)), block(kWave);
     switch (a.K) {
-        case 1: hipLaunchKernelGGL(k_combine<1>, grid, block, 0, s, a); break;
-        case 2: hipLaunchKernelGGL(k_combine<2>, grid, block, 0, s, a); break;
-        case 3: hipLaunchKernelGGL(k_combine<3>, grid, block, 0, s, a); break;
-        case 4: hipLaunchKernelGGL(k_combine<4>, grid, block, 0, s, a); break;
-        case 5: hipLaunchKernelGGL(k_combine<5>, grid, block, 0, s, a); break;
-        case 6: hipLaunchKernelGGL(k_combine<6>, grid, block, 0, s, a); break;
-        case 7: hipLaunchKernelGGL(k_combine<7>, grid, block, 0, s, a); break;
-        case 8: hipLaunchKernelGGL(k_combine<8>, grid, block, 0, s, a); break;
-        case 9: hipLaunchKernelGGL(k_combine<9>, grid, block, 0, s, a); break;
-        case 10: hipLaunchKernelGGL(k_combine<10>, grid, block, 0, s, a); break;
-        case 11: hipLaunchKernelGGL(k_combine<11>, grid, block, 0, s, a); break;
-        case 12: hipLaunchKernelGGL(k_combine<12>, grid, block, 0, s, a); break;
-        case 13: hipLaunchKernelGGL(k_combine<13>, grid, block, 0, s, a); break;
-        case 14: hipLaunchKernelGGL(k_combine<14>, grid, block, 0, s, a); break;
-        case 15: hipLaunchKernelGGL(k_combine<15>, grid, block, 0, s, a); break;
-        case 16: hipLaunchKernelGGL(k_combine<16>, grid, block, 0, s, a); break;
+        case 1: hipLaunchKernelGGL(k_combine<1>, grid, block, 0, s, a, nchunk); break;
+        case 2: hipLaunchKernelGGL(k_combine<2>, grid, block, 0, s, a, nchunk); break;
+        case 3: hipLaunchKernelGGL(k_combine<3>, grid, block, 0, s, a, nchunk); break;
+        case 4: hipLaunchKernelGGL(k_combine<4>, grid, block, 0, s, a, nchunk); break;
+        case 5: hipLaunchKernelGGL(k_combine<5>, grid, block, 0, s, a, nchunk); break;
+        case 6: hipLaunchKernelGGL(k_combine<6>, grid, block, 0, s, a, nchunk); break;
+        case 7: hipLaunchKernelGGL(k_combine<7>, grid, block, 0, s, a, nchunk); break;
+        case 8: hipLaunchKernelGGL(k_combine<8>, grid, block, 0, s, a, nchunk); break;
+        case 9: hipLaunchKernelGGL(k_combine<9>, grid, block, 0, s, a, nchunk); break;
+        case 10: hipLaunchKernelGGL(k_combine<10>, grid, block, 0, s, a, nchunk); break;
+        case 11: hipLaunchKernelGGL(k_combine<11>, grid, block, 0, s, a, nchunk); break;
+        case 12: hipLaunchKernelGGL(k_combine<12>, grid, block, 0, s, a, nchunk); break;
+        case 13: hipLaunchKernelGGL(k_combine<13>, grid, block, 0, s, a, nchunk); break;
+        case 14: hipLaunchKernelGGL(k_combine<14>, grid, block, 0, s, a, nchunk); break;
+        case 15: hipLaunchKernelGGL(k_combine<15>, grid, block, 0, s, a, nchunk); break;
+        case 16: hipLaunchKernelGGL(k_combine<16>, grid, block, 0, s, a, nchunk); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

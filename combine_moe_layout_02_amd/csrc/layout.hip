@@ -19,9 +19,11 @@
 // Two variants:
 //   fused  (S*K <= 16384): one 1024-thread workgroup does everything in one
 //          launch (decode-sized batches).
-//   multi  : k_layout_local ranks 4096-entry tiles per workgroup and writes a
-//          per-tile histogram; k_layout_scan (one workgroup) scans tiles and
-//          experts; k_layout_final turns tile ranks into rows.
+//   multi  : k_layout_local ranks 4096-entry tiles, one workgroup per tile, and
+//          writes a per-tile histogram; k_layout_place (one workgroup per tile
+//          again) rebuilds the expert offsets from all tile histograms --
+//          cheaper than a separate scan launch -- and turns tile ranks into
+//          rows.
 #include "moe_kernels.h"
 
 namespace moe {
@@ -67,10 +69,14 @@ __device__ __forceinline__ int column_scan(unsigned short *s_cnt, int E, int e) 
 }
 
 // From per-expert counts (thread e < E holds count e): placed rows, padded
-// segment lengths, their exclusive scans, and every output that depends only
-// on counts.  Also marks padding rows and the unused tail with src = -1.
-// Called by all 1024 threads; returns this thread's capacity flag.
-__device__ int finish_counts(const LayoutArgs &a, int cnt, int *s_off, int *s_pex, int2 *s_tmp) {
+// segment lengths and their exclusive scans (into s_off / s_pex).  With
+// `write_outputs`, also every output that depends only on counts.  Marks
+// padding rows and the unused tail with src = -1: this workgroup takes part
+// `part` of `parts` (experts e with e % parts == part, and every parts-th
+// 1024-row slice of the tail).  Called by all 1024 threads; returns this
+// thread's capacity flag.
+__device__ int finish_counts(const LayoutArgs &a, int cnt, int *s_off, int *s_pex, int2 *s_tmp,
+                             bool write_outputs, int part, int parts) {
     const int tid = threadIdx.x;
     const bool is_e = tid < a.E;
     int placed = is_e ? cnt : 0, seg = placed, flags = 0;
@@ -87,28 +93,33 @@ __device__ int finish_counts(const LayoutArgs &a, int cnt, int *s_off, int *s_pe
     if (is_e) {
         s_off[tid] = ex.x;
         s_pex[tid] = ex.y;
-        a.tpe[tid] = placed;
-        a.eoff[tid] = ex.x;
     }
     if (tid == 0) {
         s_off[a.E] = total.x;
         s_pex[a.E] = total.y;
-        a.eoff[a.E] = total.x;
     }
     __syncthreads();
-    const int epr = a.E / a.R;
-    if (tid < a.R) {
-        a.roff[tid] = s_off[tid * epr];
-        a.tpr[tid] = s_pex[(tid + 1) * epr] - s_pex[tid * epr];
+    if (write_outputs) {
+        if (is_e) {
+            a.tpe[tid] = placed;
+            a.eoff[tid] = ex.x;
+        }
+        if (tid == 0) a.eoff[a.E] = total.x;
+        const int epr = a.E / a.R;
+        if (tid < a.R) {
+            a.roff[tid] = s_off[tid * epr];
+            a.tpr[tid] = s_pex[(tid + 1) * epr] - s_pex[tid * epr];
+        }
+        if (tid == 0) a.roff[a.R] = s_off[a.E];
     }
-    if (tid == 0) a.roff[a.R] = s_off[a.E];
     const int wave = tid / kWave, lane = tid & (kWave - 1);
-    for (int e = wave; e < a.E; e += kLayoutWaves) {
+    for (int e = part + wave * parts; e < a.E; e += kLayoutWaves * parts) {
         const int beg = s_off[e] + (s_pex[e + 1] - s_pex[e]);
         const int end = s_off[e + 1];
         for (int r = beg + lane; r < end; r += kWave) a.src[r] = -1;
     }
-    for (int r = s_off[a.E] + tid; r < a.max_recv; r += kLayoutThreads) a.src[r] = -1;
+    for (int r = s_off[a.E] + part * kLayoutThreads + tid; r < a.max_recv; r += kLayoutThreads * parts)
+        a.src[r] = -1;
     return flags;
 }
 
@@ -128,7 +139,7 @@ __global__ __launch_bounds__(kLayoutThreads) void k_layout_fused(LayoutArgs a) {
     wave_rank<J>(a.idx, a.N, a.E, a.nbits, base, s_cnt + wave * a.E, key, local, flags);
     __syncthreads();
     const int cnt = tid < a.E ? column_scan(s_cnt, a.E, tid) : 0;
-    flags |= finish_counts(a, cnt, s_off, s_pex, s_tmp);  // synchronises the workgroup
+    flags |= finish_counts(a, cnt, s_off, s_pex, s_tmp, true, 0, 1);  // synchronises the workgroup
 
 #pragma unroll
     for (int j = 0; j < J; ++j) {
@@ -172,52 +183,56 @@ __global__ __launch_bounds__(kLayoutThreads) void k_layout_local(LayoutArgs a) {
     if (tid == 0) a.blk_flags[blockIdx.x] = s_flags;
 }
 
-__global__ __launch_bounds__(kLayoutThreads) void k_layout_scan(LayoutArgs a) {
-    __shared__ int s_off[kMaxE + 1], s_pex[kMaxE + 1];
+// Placement pass of the multi-workgroup layout; workgroup b owns tile b.
+__global__ __launch_bounds__(kLayoutThreads) void k_layout_place(LayoutArgs a) {
+    __shared__ int s_off[kMaxE + 1], s_pex[kMaxE + 1], s_pre[kMaxE];
     __shared__ int2 s_tmp[kLayoutWaves];
     __shared__ int s_flags;
-    const int tid = threadIdx.x;
+    const int tid = threadIdx.x, b = blockIdx.x;
     if (tid == 0) s_flags = 0;
     int cnt = 0;
     if (tid < a.E) {
-        // tile histograms -> exclusive prefixes over tiles, in tile order
-        int run = 0, b = 0;
-        for (; b + 8 <= a.nblk; b += 8) {
+        // expert tid: entries in tiles before b (in tile order), and in all tiles
+        int pre = 0, t = 0;
+        for (; t + 8 <= a.nblk; t += 8) {
             int c[8];
 #pragma unroll
-            for (int u = 0; u < 8; ++u) c[u] = a.blk_hist[static_cast<size_t>(b + u) * a.E + tid];
+            for (int u = 0; u < 8; ++u) c[u] = a.blk_hist[static_cast<size_t>(t + u) * a.E + tid];
 #pragma unroll
             for (int u = 0; u < 8; ++u) {
-                a.blk_hist[static_cast<size_t>(b + u) * a.E + tid] = run;
-                run += c[u];
+                pre += (t + u < b) ? c[u] : 0;
+                cnt += c[u];
             }
         }
-        for (; b < a.nblk; ++b) {
-            const int c = a.blk_hist[static_cast<size_t>(b) * a.E + tid];
-            a.blk_hist[static_cast<size_t>(b) * a.E + tid] = run;
-            run += c;
+        for (; t < a.nblk; ++t) {
+            const int c = a.blk_hist[static_cast<size_t>(t) * a.E + tid];
+            pre += (t < b) ? c : 0;
+            cnt += c;
         }
-        cnt = run;
+        s_pre[tid] = pre;
     }
     int flags = 0;
-    for (int b = tid; b < a.nblk; b += kLayoutThreads) flags |= a.blk_flags[b];
+    if (b == 0)
+        for (int t = tid; t < a.nblk; t += kLayoutThreads) flags |= a.blk_flags[t];
     __syncthreads();
-    flags |= finish_counts(a, cnt, s_off, s_pex, s_tmp);
-    if (flags) atomicOr(&s_flags, flags);
-    __syncthreads();
-    if (tid == 0) a.status[0] = s_flags;
-}
-
-__global__ __launch_bounds__(256) void k_layout_final(LayoutArgs a) {
-    const int stride = gridDim.x * blockDim.x;
-    for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < a.N; i += stride) {
+    flags |= finish_counts(a, cnt, s_off, s_pex, s_tmp, b == 0, b, a.nblk);
+    // tile b's entries: tile rank -> row
+#pragma unroll
+    for (int j = 0; j < kMultiJ; ++j) {
+        const int i = b * kMultiTile + j * kLayoutThreads + tid;
+        if (i >= a.N) break;
         const int e = a.idx[i];
         if (e < 0 || e >= a.E) continue;  // already -1
-        const int within = a.blk_hist[static_cast<size_t>(i / kMultiTile) * a.E + e] + a.pos[i];
+        const int within = s_pre[e] + a.pos[i];
         int p = -1;
-        if (!(a.pad_mode == PAD_CAPACITY && within >= a.pad_rows)) p = a.eoff[e] + within;
+        if (!(a.pad_mode == PAD_CAPACITY && within >= a.pad_rows)) p = s_off[e] + within;
         a.pos[i] = p;
         if (p >= 0) a.src[p] = i;
+    }
+    if (b == 0) {
+        if (flags) atomicOr(&s_flags, flags);
+        __syncthreads();
+        if (tid == 0) a.status[0] = s_flags;
     }
 }
 
@@ -252,11 +267,7 @@ hipError_t launch_layout(const LayoutArgs &a_in, hipStream_t s) {
     hipLaunchKernelGGL(k_layout_local<kMultiJ>, dim3(a.nblk), dim3(kLayoutThreads), lds, s, a);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    hipLaunchKernelGGL(k_layout_scan, dim3(1), dim3(kLayoutThreads), 0, s, a);
-    err = hipGetLastError();
-    if (err != hipSuccess) return err;
-    const int blocks = static_cast<int>((static_cast<int64_t>(a.N) + 255) / 256 < 2048 ? (a.N + 255) / 256 : 2048);
-    hipLaunchKernelGGL(k_layout_final, dim3(blocks), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(k_layout_place, dim3(a.nblk), dim3(kLayoutThreads), 0, s, a);
     return hipGetLastError();
 }
 

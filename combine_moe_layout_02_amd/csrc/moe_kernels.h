@@ -58,6 +58,12 @@ hipError_t launch_combine(const CombineArgs &a, hipStream_t stream);
 // device helpers
 // ---------------------------------------------------------------------------
 
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));  // one 16-byte vector
+
+// the two bf16 halves of a 32-bit word, widened exactly to fp32
+__device__ __forceinline__ float bf16_lo(unsigned int w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(unsigned int w) { return __uint_as_float(w & 0xFFFF0000u); }
+
 // Number of set bits of `m` below this lane (v_mbcnt_lo / v_mbcnt_hi).
 __device__ __forceinline__ int lanes_below(uint64_t m) {
     return __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(m >> 32),
