@@ -230,3 +230,91 @@ def moe_combine(desc: LayoutDesc, layout: Layout, expert_out: torch.Tensor, w=No
     if rc != MOE_OK:
         raise MoeError(rc, "moe_combine")
     return out
+
+
+# ---------------------------------------------------------------------------
+# Static-shape buffer: validate once, then bare C calls
+# ---------------------------------------------------------------------------
+
+class Buffer:
+    """All device buffers of one batch shape, allocated once (static shapes, no
+    host sync between layers), with prepared C calls.
+
+    Mirrors the call shape of MoonEP's Buffer (MoonEP article, basic usage):
+    ``dispatch(hidden, topk_w, topk_idx)`` returns the expert-grouped rows,
+    their per-row weights and the per-expert offsets; ``combine(expert_out)``
+    returns the token-order result.  Every call is asynchronous on the current
+    stream (or the one given); outputs are views of the buffer's own tensors
+    and are overwritten by the next call.
+    """
+
+    def __init__(self, S: int, H: int, K: int, E: int, R: int, fp8: bool = False,
+                 pad_mode: int = MOE_PAD_NONE, pad_rows: int = 0, device="cuda", shared: bool = False):
+        self.desc = LayoutDesc(S, K, E, R, pad_mode, pad_rows)
+        self.rows = moe_max_recv_rows(self.desc)
+        if self.rows < 0 or H < 8 or H % 8 or (fp8 and H % 128):
+            raise MoeError(MOE_ERR_SHAPE, "Buffer")
+        dev = torch.device(device)
+        if dev.type == "cuda" and dev.index is None:
+            dev = torch.device("cuda", torch.cuda.current_device())
+        self.H, self.fp8, self.device = H, fp8, dev
+        self.layout = alloc_layout(self.desc, dev)
+        self.recv = torch.empty((self.rows, H), dtype=torch.uint8 if fp8 else torch.bfloat16, device=dev)
+        self.recv_scales = torch.empty((self.rows, H // 128), dtype=torch.float32, device=dev) if fp8 else None
+        self.recv_w = torch.empty(self.rows, dtype=torch.float32, device=dev)
+        self.out = torch.empty((S, H), dtype=torch.bfloat16, device=dev)
+        self._d = self.desc.c()
+        self._b = self.layout.c()
+        self._dp = ctypes.byref(self._d)
+        self._bp = ctypes.byref(self._b)
+        ws = self.layout.workspace
+        self._ws = (_ptr(ws), 0 if ws is None else ws.numel())
+        self._recv = _ptr(self.recv)
+        self._scales = _ptr(self.recv_scales)
+        self._recv_w = _ptr(self.recv_w)
+        self._out = _ptr(self.out)
+
+    def _inputs(self, hidden, topk_idx, topk_w):
+        S, K = self.desc.S, self.desc.K
+        _check(topk_idx, "topk_idx", torch.int32, (S, K), self.device)
+        _check(hidden, "hidden", torch.bfloat16, (S, self.H), self.device)
+        _check(topk_w, "topk_w", torch.float32, (S, K), self.device)
+
+    def layout_call(self, topk_idx, stream=None, check=True):
+        if check:
+            _check(topk_idx, "topk_idx", torch.int32, (self.desc.S, self.desc.K), self.device)
+        rc = _lib.moe_layout(self._dp, _ptr(topk_idx), self._bp, self._ws[0], self._ws[1],
+                             _stream(stream, self.device))
+        if rc != MOE_OK:
+            raise MoeError(rc, "moe_layout")
+
+    def dispatch_call(self, hidden, topk_idx=None, topk_w=None, stream=None, check=True):
+        if check:
+            self._inputs(hidden, topk_idx, topk_w)
+        rc = _lib.moe_dispatch(self._dp, self._bp, _ptr(hidden), self.H, _ptr(topk_idx), _ptr(topk_w),
+                               1 if self.fp8 else 0, self._recv, self._scales,
+                               self._recv_w if topk_w is not None else None, _stream(stream, self.device))
+        if rc != MOE_OK:
+            raise MoeError(rc, "moe_dispatch")
+
+    def combine_call(self, expert_out, w=None, shared_out=None, stream=None, check=True):
+        if check:
+            _check(expert_out, "expert_out", torch.bfloat16, (self.rows, self.H), self.device)
+            _check(w, "w", torch.float32, (self.desc.S, self.desc.K), self.device)
+            _check(shared_out, "shared_out", torch.bfloat16, (self.desc.S, self.H), self.device)
+        rc = _lib.moe_combine(self._dp, self._bp, _ptr(expert_out), self.H, _ptr(w), _ptr(shared_out),
+                              self._out, _stream(stream, self.device))
+        if rc != MOE_OK:
+            raise MoeError(rc, "moe_combine")
+
+    def dispatch(self, hidden, topk_w, topk_idx, stream=None):
+        """Layout + dispatch.  Returns (recv, recv_w, expert_offset, recv_scales)."""
+        self._inputs(hidden, topk_idx, topk_w)
+        self.layout_call(topk_idx, stream, check=False)
+        self.dispatch_call(hidden, topk_idx, topk_w, stream, check=False)
+        return self.recv, self.recv_w, self.layout.expert_offset, self.recv_scales
+
+    def combine(self, expert_out, w=None, shared_out=None, stream=None):
+        """Route-weighted gather back to token order.  Returns out [S,H] bf16."""
+        self.combine_call(expert_out, w, shared_out, stream)
+        return self.out
