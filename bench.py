@@ -132,9 +132,16 @@ class Run:
     def combine_call(self):
         self.buf.combine_call(self.expert_out, self.topk_w, self.shared, check=False)
 
+    def layout_dispatch_call(self):
+        self.buf.layout_dispatch_call(self.hidden, self.idx, self.topk_w, check=False)
+
     def step(self):
         self.layout_call()
         self.dispatch_call()
+        self.combine_call()
+
+    def fused_step(self):
+        self.layout_dispatch_call()
         self.combine_call()
 
     def bytes(self):
@@ -179,18 +186,18 @@ def time_steps(run, steps: int, warmup: int):
     return dict(layout_ms=lay, dispatch_ms=dis, combine_ms=com, step_ms=step_ms, wall_s=wall)
 
 
-def time_graph(run, iters: int):
-    """Layout + dispatch + combine captured once in a HIP graph, replayed."""
+def time_graph(step, iters: int):
+    """One step captured once in a HIP graph, replayed `iters` times."""
     import torch
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(s):
-        run.step()
+        step()
     torch.cuda.current_stream().wait_stream(s)
     torch.cuda.synchronize()
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
-        run.step()
+        step()
     for _ in range(10):
         graph.replay()
     torch.cuda.synchronize()
@@ -201,6 +208,39 @@ def time_graph(run, iters: int):
     b.record()
     torch.cuda.synchronize()
     return a.elapsed_time(b) / iters
+
+
+def time_calls(step, iters: int, warmup: int = 20):
+    """Average ms per step, events only at the ends of the timed region."""
+    import torch
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(iters):
+        step()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / iters
+
+
+def decode_numbers(moe, dcfg, dev, iters: int):
+    """µs per decode call (S=128): moe_layout_dispatch (one launch) + moe_combine,
+    eager and graph-replayed, and the three-call variant."""
+    drun = Run(moe, dcfg, dev)
+    dt = time_steps(drun, iters, 20)
+    fused_ms = time_calls(drun.fused_step, iters)
+    ld_ms = time_calls(drun.layout_dispatch_call, iters)
+    comb_ms = time_calls(drun.combine_call, iters)
+    g_ms = time_graph(drun.fused_step, iters)
+    return {"us_per_call": round(fused_ms * 1e3, 2),
+            "call": "moe_layout_dispatch (one launch) + moe_combine",
+            "layout_dispatch_us": round(ld_ms * 1e3, 2), "combine_us": round(comb_ms * 1e3, 2),
+            "graph_replay_us_per_call": round(g_ms * 1e3, 2),
+            "three_call_us_per_call": round(dt["step_ms"] * 1e3, 2),
+            "config": {"workload": "decode", "S": dcfg.S, "H": dcfg.H, "E": dcfg.E, "K": dcfg.K,
+                       "R": dcfg.R, "fp8": dcfg.fp8, "capacity": dcfg.pad_rows}}
 
 
 def cpu_baseline(cfg, budget_s: float = 12.0):
@@ -254,6 +294,8 @@ def main(argv=None):
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--calib-copy", action="store_true")
+    ap.add_argument("--only-decode", action="store_true",
+                    help="time only the decode call (S=128) and print its JSON object")
     args = ap.parse_args(argv)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -269,6 +311,9 @@ def main(argv=None):
     from workloads import CONFIGS
 
     dev = torch.device("cuda:0")
+    if args.only_decode:
+        print(json.dumps(decode_numbers(moe, CONFIGS["decode"], dev, args.decode_iters)), flush=True)
+        return
     cfg = CONFIGS[args.config]
     run = Run(moe, cfg, dev)
     lb, db, cb = run.bytes()
@@ -295,18 +340,7 @@ def main(argv=None):
              "dispatch_plus_combine_frac_of_peak": round(dc_gbps / HBM_PEAK_GBPS, 4),
              "bytes": {"layout": lb, "dispatch": db, "combine": cb}, "wall_s_timed": round(t["wall_s"], 3)}
 
-    decode = None
-    if not args.no_decode:
-        dcfg = CONFIGS["decode"]
-        drun = Run(moe, dcfg, dev)
-        dt = time_steps(drun, args.decode_iters, 20)
-        g_ms = time_graph(drun, args.decode_iters)
-        decode = {"us_per_call": round(dt["step_ms"] * 1e3, 2), "layout_us": round(dt["layout_ms"] * 1e3, 2),
-                  "dispatch_us": round(dt["dispatch_ms"] * 1e3, 2), "combine_us": round(dt["combine_ms"] * 1e3, 2),
-                  "graph_replay_us_per_call": round(g_ms * 1e3, 2),
-                  "config": {"workload": "decode", "S": dcfg.S, "H": dcfg.H, "E": dcfg.E, "K": dcfg.K,
-                             "R": dcfg.R, "fp8": True, "capacity": dcfg.pad_rows}}
-        del drun
+    decode = None if args.no_decode else decode_numbers(moe, CONFIGS["decode"], dev, args.decode_iters)
 
     cpu = None
     if not args.no_cpu_baseline:

@@ -23,7 +23,7 @@ MOE_PAD_NONE, MOE_PAD_MULTIPLE, MOE_PAD_CAPACITY = 0, 1, 2
 MOE_FLAG_BAD_EXPERT, MOE_FLAG_CAPACITY = 1, 2
 
 EXPORTED = ("moe_max_recv_rows", "moe_layout_workspace_bytes", "moe_layout", "moe_dispatch",
-            "moe_combine", "moe_status_str")
+            "moe_layout_dispatch", "moe_combine", "moe_status_str")
 
 
 class MoeError(RuntimeError):
@@ -58,6 +58,9 @@ def _load():
     L.moe_layout.restype = ctypes.c_int
     L.moe_dispatch.argtypes = [D, B, P, ctypes.c_int32, P, P, ctypes.c_int32, P, P, P, P]
     L.moe_dispatch.restype = ctypes.c_int
+    L.moe_layout_dispatch.argtypes = [D, P, B, P, ctypes.c_size_t, P, ctypes.c_int32, P, ctypes.c_int32,
+                                      P, P, P, P]
+    L.moe_layout_dispatch.restype = ctypes.c_int
     L.moe_combine.argtypes = [D, B, P, ctypes.c_int32, P, P, P, P]
     L.moe_combine.restype = ctypes.c_int
     L.moe_status_str.argtypes = [ctypes.c_int32]
@@ -212,6 +215,44 @@ def moe_dispatch(desc: LayoutDesc, layout: Layout, hidden: torch.Tensor, topk_id
     return recv, (recv_scales if fp8 else None), recv_w
 
 
+def moe_layout_dispatch(desc: LayoutDesc, topk_idx: torch.Tensor, hidden: torch.Tensor, topk_w=None,
+                        fp8: bool = False, layout: Optional[Layout] = None, recv=None, recv_scales=None,
+                        recv_w=None, stream=None):
+    """moe_layout + moe_dispatch in one call (one launch for S*K <= 4096).
+    Returns (layout, recv, recv_scales or None, recv_w or None)."""
+    dev = hidden.device
+    H = hidden.shape[1]
+    rows = moe_max_recv_rows(desc)
+    _check(topk_idx, "topk_idx", torch.int32, (desc.S, desc.K))
+    _check(hidden, "hidden", torch.bfloat16, (desc.S, H))
+    _check(topk_w, "topk_w", torch.float32, (desc.S, desc.K))
+    if layout is None:
+        layout = alloc_layout(desc, dev)
+    if recv is None:
+        recv = torch.empty((rows, H), dtype=torch.uint8 if fp8 else torch.bfloat16, device=dev)
+    if fp8 and recv_scales is None:
+        recv_scales = torch.empty((rows, H // 128), dtype=torch.float32, device=dev)
+    if recv_w is None and topk_w is not None:
+        recv_w = torch.empty(rows, dtype=torch.float32, device=dev)
+    _check(recv, "recv", (torch.uint8, torch.float8_e4m3fn) if fp8 else torch.bfloat16)
+    if recv.shape[0] < rows or recv.shape[-1] != H:
+        raise ValueError("recv must hold moe_max_recv_rows rows of H channels")
+    if fp8:
+        _check(recv_scales, "recv_scales", torch.float32)
+        if recv_scales.shape[0] < rows or recv_scales.shape[-1] != H // 128:
+            raise ValueError("recv_scales must be [max_recv, H/128]")
+    _check(recv_w, "recv_w", torch.float32)
+    ws = layout.workspace
+    d, b = desc.c(), layout.c()
+    rc = _lib.moe_layout_dispatch(ctypes.byref(d), _ptr(topk_idx), ctypes.byref(b), _ptr(ws),
+                                  0 if ws is None else ws.numel(), _ptr(hidden), H, _ptr(topk_w),
+                                  1 if fp8 else 0, _ptr(recv), _ptr(recv_scales if fp8 else None), _ptr(recv_w),
+                                  _stream(stream, dev))
+    if rc != MOE_OK:
+        raise MoeError(rc, "moe_layout_dispatch")
+    return layout, recv, (recv_scales if fp8 else None), recv_w
+
+
 def moe_combine(desc: LayoutDesc, layout: Layout, expert_out: torch.Tensor, w=None, shared_out=None,
                 out=None, stream=None) -> torch.Tensor:
     dev = expert_out.device
@@ -297,6 +338,16 @@ class Buffer:
         if rc != MOE_OK:
             raise MoeError(rc, "moe_dispatch")
 
+    def layout_dispatch_call(self, hidden, topk_idx, topk_w=None, stream=None, check=True):
+        """moe_layout_dispatch: one launch for decode-sized batches."""
+        if check:
+            self._inputs(hidden, topk_idx, topk_w)
+        rc = _lib.moe_layout_dispatch(self._dp, _ptr(topk_idx), self._bp, self._ws[0], self._ws[1], _ptr(hidden),
+                                      self.H, _ptr(topk_w), 1 if self.fp8 else 0, self._recv, self._scales,
+                                      self._recv_w if topk_w is not None else None, _stream(stream, self.device))
+        if rc != MOE_OK:
+            raise MoeError(rc, "moe_layout_dispatch")
+
     def combine_call(self, expert_out, w=None, shared_out=None, stream=None, check=True):
         if check:
             _check(expert_out, "expert_out", torch.bfloat16, (self.rows, self.H), self.device)
@@ -309,9 +360,7 @@ class Buffer:
 
     def dispatch(self, hidden, topk_w, topk_idx, stream=None):
         """Layout + dispatch.  Returns (recv, recv_w, expert_offset, recv_scales)."""
-        self._inputs(hidden, topk_idx, topk_w)
-        self.layout_call(topk_idx, stream, check=False)
-        self.dispatch_call(hidden, topk_idx, topk_w, stream, check=False)
+        self.layout_dispatch_call(hidden, topk_idx, topk_w, stream)
         return self.recv, self.recv_w, self.layout.expert_offset, self.recv_scales
 
     def combine(self, expert_out, w=None, shared_out=None, stream=None):

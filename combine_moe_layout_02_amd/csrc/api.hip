@@ -49,8 +49,13 @@ size_t moe_layout_workspace_bytes(const moe_layout_desc *desc) {
     return moe::layout_workspace_bytes(static_cast<int64_t>(desc->S) * desc->K, desc->E);
 }
 
-moe_status moe_layout(const moe_layout_desc *desc, const int32_t *topk_idx, const moe_layout_bufs *out,
-                      void *workspace, size_t workspace_bytes, void *stream) {
+}  // extern "C"
+
+namespace {
+
+// Checks shared by moe_layout and moe_layout_dispatch; fills the kernel args.
+moe_status prepare_layout(const moe_layout_desc *desc, const int32_t *topk_idx, const moe_layout_bufs *out,
+                          void *workspace, size_t workspace_bytes, moe::LayoutArgs &a) {
     if (desc == nullptr || out == nullptr) return MOE_ERR_NULL;
     if (!desc_ok(desc) || max_rows(desc) < 0) return MOE_ERR_SHAPE;
     const int64_t n = static_cast<int64_t>(desc->S) * desc->K;
@@ -66,8 +71,7 @@ moe_status moe_layout(const moe_layout_desc *desc, const int32_t *topk_idx, cons
     const size_t need = moe::layout_workspace_bytes(n, desc->E);
     if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return MOE_ERR_WORKSPACE;
     if (need > 0 && !aligned(workspace, 16)) return MOE_ERR_ALIGN;
-
-    moe::LayoutArgs a{};
+    a = moe::LayoutArgs{};
     a.idx = topk_idx;
     a.N = static_cast<int32_t>(n);
     a.E = desc->E;
@@ -84,6 +88,42 @@ moe_status moe_layout(const moe_layout_desc *desc, const int32_t *topk_idx, cons
     a.src = out->src;
     a.status = out->status;
     a.blk_hist = static_cast<int32_t *>(workspace);
+    return MOE_OK;
+}
+
+// Checks shared by moe_dispatch and moe_layout_dispatch (pos is checked by the
+// caller where it is an input).
+moe_status prepare_dispatch(const moe_layout_desc *desc, const void *hidden, int32_t H, const float *topk_w,
+                            int32_t fp8, void *recv, float *recv_scales, float *recv_w, moe::DispatchArgs &a) {
+    if (!desc_ok(desc) || max_rows(desc) < 0 || H < 8 || H % 8 != 0) return MOE_ERR_SHAPE;
+    if (fp8 && H % 128 != 0) return MOE_ERR_SHAPE;
+    if ((H / (fp8 ? 16 : 8) + moe::kWave - 1) / moe::kWave > 65535) return MOE_ERR_SHAPE;  // grid.y
+    if (desc->S > 0 && (hidden == nullptr || recv == nullptr)) return MOE_ERR_NULL;
+    if (desc->S > 0 && fp8 && recv_scales == nullptr) return MOE_ERR_NULL;
+    if (!aligned(hidden, 16) || !aligned(recv, 16) || !aligned(recv_scales, 4) || !aligned(recv_w, 4) ||
+        !aligned(topk_w, 4))
+        return MOE_ERR_ALIGN;
+    a = moe::DispatchArgs{};
+    a.hidden = hidden;
+    a.S = desc->S;
+    a.H = H;
+    a.K = desc->K;
+    a.topk_w = topk_w;
+    a.recv = recv;
+    a.recv_scales = recv_scales;
+    a.recv_w = recv_w;
+    return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status moe_layout(const moe_layout_desc *desc, const int32_t *topk_idx, const moe_layout_bufs *out,
+                      void *workspace, size_t workspace_bytes, void *stream) {
+    moe::LayoutArgs a;
+    const moe_status st = prepare_layout(desc, topk_idx, out, workspace, workspace_bytes, a);
+    if (st != MOE_OK) return st;
     return moe::launch_layout(a, static_cast<hipStream_t>(stream)) == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 
@@ -92,27 +132,38 @@ moe_status moe_dispatch(const moe_layout_desc *desc, const moe_layout_bufs *layo
                         float *recv_scales, float *recv_w, void *stream) {
     (void)topk_idx;  // already folded into layout->pos
     if (desc == nullptr || layout == nullptr) return MOE_ERR_NULL;
-    if (!desc_ok(desc) || max_rows(desc) < 0 || H < 8 || H % 8 != 0) return MOE_ERR_SHAPE;
-    if (fp8 && H % 128 != 0) return MOE_ERR_SHAPE;
-    if ((H / (fp8 ? 16 : 8) + moe::kWave - 1) / moe::kWave > 65535) return MOE_ERR_SHAPE;  // grid.y
+    moe::DispatchArgs a;
+    const moe_status st = prepare_dispatch(desc, hidden, H, topk_w, fp8, recv, recv_scales, recv_w, a);
+    if (st != MOE_OK) return st;
     if (desc->S == 0) return MOE_OK;
-    if (hidden == nullptr || recv == nullptr || layout->pos == nullptr) return MOE_ERR_NULL;
-    if (fp8 && recv_scales == nullptr) return MOE_ERR_NULL;
-    if (!aligned(hidden, 16) || !aligned(recv, 16) || !aligned(layout->pos, 4) || !aligned(recv_scales, 4) ||
-        !aligned(recv_w, 4) || !aligned(topk_w, 4))
-        return MOE_ERR_ALIGN;
-    moe::DispatchArgs a{};
-    a.hidden = hidden;
-    a.S = desc->S;
-    a.H = H;
-    a.K = desc->K;
+    if (layout->pos == nullptr) return MOE_ERR_NULL;
+    if (!aligned(layout->pos, 4)) return MOE_ERR_ALIGN;
     a.pos = layout->pos;
-    a.topk_w = topk_w;
-    a.recv = recv;
-    a.recv_scales = recv_scales;
-    a.recv_w = recv_w;
     const hipStream_t s = static_cast<hipStream_t>(stream);
     const hipError_t err = fp8 ? moe::launch_dispatch_fp8(a, s) : moe::launch_dispatch_bf16(a, s);
+    return err == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+moe_status moe_layout_dispatch(const moe_layout_desc *desc, const int32_t *topk_idx, const moe_layout_bufs *out,
+                               void *workspace, size_t workspace_bytes, const void *hidden, int32_t H,
+                               const float *topk_w, int32_t fp8, void *recv, float *recv_scales, float *recv_w,
+                               void *stream) {
+    moe::LayoutArgs la;
+    moe_status st = prepare_layout(desc, topk_idx, out, workspace, workspace_bytes, la);
+    if (st != MOE_OK) return st;
+    moe::DispatchArgs da;
+    st = prepare_dispatch(desc, hidden, H, topk_w, fp8, recv, recv_scales, recv_w, da);
+    if (st != MOE_OK) return st;
+    da.pos = out->pos;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t err;
+    if (la.N > 0 && la.N <= moe::kFusedDispatchMaxN) {
+        err = moe::launch_layout_dispatch_small(la, da, fp8 != 0, s);
+    } else {
+        err = moe::launch_layout(la, s);
+        if (err == hipSuccess && desc->S > 0)
+            err = fp8 ? moe::launch_dispatch_fp8(da, s) : moe::launch_dispatch_bf16(da, s);
+    }
     return err == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 

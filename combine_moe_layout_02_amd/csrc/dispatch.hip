@@ -63,32 +63,8 @@ __global__ __launch_bounds__(kWave) void k_dispatch_fp8(DispatchArgs a) {
         lo = hid[2 * g];
         hi = hid[2 * g + 1];
     }
-    float f[16];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        f[2 * i] = bf16_lo(lo[i]);
-        f[2 * i + 1] = bf16_hi(lo[i]);
-        f[8 + 2 * i] = bf16_lo(hi[i]);
-        f[8 + 2 * i + 1] = bf16_hi(hi[i]);
-    }
-    float amax = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(f[i]));
-    // the 8 lanes of one 128-channel block share their maximum
-    amax = fmaxf(amax, __shfl_xor(amax, 1, kWave));
-    amax = fmaxf(amax, __shfl_xor(amax, 2, kWave));
-    amax = fmaxf(amax, __shfl_xor(amax, 4, kWave));
-    const float scale = amax / 448.0f;
-
-    u32x4 q = {0u, 0u, 0u, 0u};
-    if (amax != 0.0f) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            int w = __builtin_amdgcn_cvt_pk_fp8_f32(f[4 * i] / scale, f[4 * i + 1] / scale, 0, false);
-            w = __builtin_amdgcn_cvt_pk_fp8_f32(f[4 * i + 2] / scale, f[4 * i + 3] / scale, w, true);
-            q[i] = static_cast<unsigned int>(w);
-        }
-    }
+    float scale;
+    const u32x4 q = quantize16_e4m3(lo, hi, scale);
     const int nsc = a.H / 128;
     u32x4 *__restrict__ recv = static_cast<u32x4 *>(a.recv);
     if (active) {

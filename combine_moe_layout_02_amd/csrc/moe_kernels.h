@@ -48,7 +48,13 @@ struct CombineArgs {
     void *out;            // [S,H] bf16
 };
 
+// single-launch layout + dispatch for batches of at most this many entries
+constexpr int kFusedDispatchMaxN = 4096;
+constexpr int kFusedDispatchThreads = 256;
+
 size_t layout_workspace_bytes(int64_t N, int E);
+hipError_t launch_layout_dispatch_small(const LayoutArgs &la, const DispatchArgs &da, bool fp8,
+                                        hipStream_t stream);
 hipError_t launch_layout(const LayoutArgs &a, hipStream_t stream);
 hipError_t launch_dispatch_bf16(const DispatchArgs &a, hipStream_t stream);
 hipError_t launch_dispatch_fp8(const DispatchArgs &a, hipStream_t stream);
@@ -63,6 +69,42 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));  // one 16-byte 
 // the two bf16 halves of a 32-bit word, widened exactly to fp32
 __device__ __forceinline__ float bf16_lo(unsigned int w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(unsigned int w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// FP8 quantisation of one lane's 16 consecutive bf16 channels (two 16-byte
+// vectors), as part of the 8-lane group that holds one 128-channel block:
+// amax over the block (cross-lane swaps inside the group), scale = amax / 448
+// (correctly rounded fp32 division), code = E4M3(x / scale) (correctly rounded
+// division, then v_cvt_pk_fp8_f32: OCP E4M3, round to nearest even).  An
+// all-zero block gives scale 0 and codes 0.  Every lane of the wave must call
+// it (the swaps are wave-wide); groups are aligned to 8 lanes.
+__device__ __forceinline__ u32x4 quantize16_e4m3(u32x4 lo, u32x4 hi, float &scale_out) {
+    float f[16];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        f[2 * i] = bf16_lo(lo[i]);
+        f[2 * i + 1] = bf16_hi(lo[i]);
+        f[8 + 2 * i] = bf16_lo(hi[i]);
+        f[8 + 2 * i + 1] = bf16_hi(hi[i]);
+    }
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(f[i]));
+    amax = fmaxf(amax, __shfl_xor(amax, 1, kWave));
+    amax = fmaxf(amax, __shfl_xor(amax, 2, kWave));
+    amax = fmaxf(amax, __shfl_xor(amax, 4, kWave));
+    const float scale = amax / 448.0f;
+    u32x4 q = {0u, 0u, 0u, 0u};
+    if (amax != 0.0f) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            int w = __builtin_amdgcn_cvt_pk_fp8_f32(f[4 * i] / scale, f[4 * i + 1] / scale, 0, false);
+            w = __builtin_amdgcn_cvt_pk_fp8_f32(f[4 * i + 2] / scale, f[4 * i + 3] / scale, w, true);
+            q[i] = static_cast<unsigned int>(w);
+        }
+    }
+    scale_out = scale;
+    return q;
+}
 
 // Number of set bits of `m` below this lane (v_mbcnt_lo / v_mbcnt_hi).
 __device__ __forceinline__ int lanes_below(uint64_t m) {
@@ -96,9 +138,10 @@ __device__ __forceinline__ int2 wave_inclusive_scan2(int2 v) {
     return v;
 }
 
-// Exclusive prefix sum of an int pair across a 1024-thread workgroup, in
-// thread order.  `s_tmp` holds kLayoutWaves entries.  Returns the prefix and
-// the workgroup total.  Contains __syncthreads: call from every thread.
+// Exclusive prefix sum of an int pair across a workgroup of WAVES waves, in
+// thread order.  `s_tmp` holds WAVES entries.  Returns the prefix and the
+// workgroup total.  Contains __syncthreads: call from every thread.
+template <int WAVES = kLayoutWaves>
 __device__ __forceinline__ int2 block_exclusive_scan2(int2 v, int2 *s_tmp, int2 &total) {
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
@@ -107,7 +150,7 @@ __device__ __forceinline__ int2 block_exclusive_scan2(int2 v, int2 *s_tmp, int2 
     __syncthreads();
     int2 before = make_int2(0, 0), all = make_int2(0, 0);
 #pragma unroll
-    for (int w = 0; w < kLayoutWaves; ++w) {
+    for (int w = 0; w < WAVES; ++w) {
         const int2 t = s_tmp[w];
         if (w < wave) { before.x += t.x; before.y += t.y; }
         all.x += t.x; all.y += t.y;

@@ -147,6 +147,19 @@ moe_status moe_dispatch(const moe_layout_desc *desc, const moe_layout_bufs *layo
                         const float *topk_w, int32_t fp8, void *recv, float *recv_scales,
                         float *recv_w, void *stream);
 
+/* Layout + dispatch in one call: the same results as moe_layout followed by
+ * moe_dispatch with these arguments (every output of both).  Batches with
+ * S*K <= 4096 (decode-sized) run as ONE kernel launch in which each workgroup
+ * rebuilds the layout counts it needs in LDS; larger batches run the two calls'
+ * kernels back to back.  Arguments as in moe_layout and moe_dispatch; the
+ * workspace rule is moe_layout's.  This is the low-latency variant for
+ * inference decoding (DeepEP analysis, feature list: low-latency kernels for
+ * decoding). */
+moe_status moe_layout_dispatch(const moe_layout_desc *desc, const int32_t *topk_idx,
+                               const moe_layout_bufs *out, void *workspace, size_t workspace_bytes,
+                               const void *hidden, int32_t H, const float *topk_w, int32_t fp8,
+                               void *recv, float *recv_scales, float *recv_w, void *stream);
+
 /* Combine: out[t,c] = bf16_rne( (fma chain over k = 0..K-1 of
  *                                w[t,k] * expert_out[pos[t,k], c], from +0.0)
  *                               + shared_out[t,c] ).

@@ -357,3 +357,66 @@ def test_graph_replay(moe):
         got = snapshot()
         for a, b in zip(got, want):
             assert torch.equal(a, b)
+
+
+FUSED = [
+    # name, S, H, E, K, R, pad_mode, pad_rows, fp8, routing
+    ("decode", 128, 7168, 256, 8, 8, PAD_CAPACITY, 128, True, "uniform"),
+    ("tiny-bf16", 256, 512, 16, 2, 4, PAD_NONE, 0, False, "uniform"),
+    ("max-fused-N4096-E1024-K16", 256, 256, 1024, 16, 8, PAD_MULTIPLE, 5, True, "uniform"),
+    ("fallback-N4104", 513, 128, 64, 8, 8, PAD_NONE, 0, True, "uniform"),
+    ("fallback-multi-N20000", 2500, 64, 32, 8, 4, PAD_MULTIPLE, 16, False, "uniform"),
+    ("capacity-overflow", 300, 1024, 16, 8, 4, PAD_CAPACITY, 100, True, "uniform"),
+    ("bad-ids", 200, 136, 32, 4, 2, PAD_NONE, 0, False, "bad"),
+    ("duplicates", 100, 8, 4, 6, 2, PAD_MULTIPLE, 3, False, "dup"),
+    ("one-token", 1, 128, 1, 1, 1, PAD_NONE, 0, True, "uniform"),
+]
+
+
+@pytest.mark.parametrize("case", FUSED, ids=[c[0] for c in FUSED])
+def test_layout_dispatch(moe, case):
+    """moe_layout_dispatch (one launch for S*K <= 4096, two otherwise) against
+    the oracle's layout + dispatch, every output bit for bit."""
+    name, S, H, E, K, R, pad_mode, pad_rows, fp8, routing = case
+    seed = 7000 + FUSED.index(case)
+    rng = np.random.default_rng(seed)
+    cfg = _case(name, S, H, E, K, R, pad_mode, pad_rows)
+    hidden = make_workload(dataclasses_replace_uniform(cfg), seed=seed).hidden
+    if routing == "uniform":
+        idx = make_workload(cfg, seed=seed).topk_idx
+    else:
+        idx = rng.integers(0, E, (S, K)).astype(np.int32)
+        if routing == "bad":
+            hit = rng.random((S, K)) < 0.02
+            idx[hit] = rng.choice([-1, E, 1 << 30], int(hit.sum()))
+    tw = rng.random((S, K)).astype(np.float32)
+    say(f"case layout-dispatch {name}: S={S} H={H} E={E} K={K} fp8={fp8}")
+    desc = moe.LayoutDesc(S, K, E, R, pad_mode, pad_rows)
+    rows = moe.moe_max_recv_rows(desc)
+    ref = oracle.layout(idx, E, R, pad_mode, pad_rows)
+    valid = ref.src >= 0
+    if fp8:
+        recv = torch.full((rows, H), POISON_U8, dtype=torch.uint8, device=DEV)
+        scales = torch.full((rows, H // 128), float("nan"), dtype=torch.float32, device=DEV)
+    else:
+        recv = torch.full((rows, H), POISON_BF16, dtype=torch.int16, device=DEV).view(torch.bfloat16)
+        scales = None
+    recv_w = torch.full((rows,), float("nan"), dtype=torch.float32, device=DEV)
+    lay, _, _, _ = moe.moe_layout_dispatch(desc, torch.from_numpy(idx).to(DEV), dev_bf16(hidden, DEV),
+                                           torch.from_numpy(tw).to(DEV), fp8=fp8, recv=recv,
+                                           recv_scales=scales, recv_w=recv_w)
+    torch.cuda.synchronize()
+    compare_layout(lay, ref, f"{name} layout")
+    if fp8:
+        rc, rs, rw = oracle.dispatch_fp8(hidden, ref.pos, rows, tw)
+        got = recv.cpu().numpy()
+        assert np.array_equal(got[valid], rc[valid])
+        assert np.array_equal(scales.cpu().numpy()[valid].view(np.uint32), rs[valid].view(np.uint32))
+        assert np.all(got[~valid] == POISON_U8)
+    else:
+        rb, rw = oracle.dispatch_bf16(hidden, ref.pos, rows, tw)
+        got = host_bits(recv)
+        assert np.array_equal(got[valid], rb[valid])
+        assert np.all(got[~valid] == POISON_BF16)
+    assert np.array_equal(recv_w.cpu().numpy()[valid].view(np.uint32), rw[valid].view(np.uint32))
+    assert np.all(np.isnan(recv_w.cpu().numpy()[~valid]))
