@@ -16,14 +16,15 @@
 // A column scan over the 16 per-wave counters then orders the waves.  Nothing
 // depends on the order in which waves or workgroups run.
 //
-// Two variants:
-//   fused  (S*K <= 16384): one 1024-thread workgroup does everything in one
-//          launch (decode-sized batches).
-//   multi  : k_layout_local ranks 4096-entry tiles, one workgroup per tile, and
-//          writes a per-tile histogram; k_layout_place (one workgroup per tile
-//          again) rebuilds the expert offsets from all tile histograms --
-//          cheaper than a separate scan launch -- and turns tile ranks into
-//          rows.
+// Two variants (thresholds measured on MI355X):
+//   single (S*K <= 2048): one 1024-thread workgroup does everything in one
+//          launch.  Above that one CU cannot issue the scattered src stores
+//          fast enough.
+//   multi  : k_layout_local ranks tiles of 1024*J entries, one workgroup per
+//          tile, and writes a per-tile histogram; k_layout_place (one
+//          workgroup per tile again) rebuilds the expert offsets from all tile
+//          histograms -- cheaper than a separate scan launch -- and turns tile
+//          ranks into rows.  Small tiles spread the scatter over more CUs.
 #include "moe_kernels.h"
 
 namespace moe {
@@ -183,7 +184,9 @@ __global__ __launch_bounds__(kLayoutThreads) void k_layout_local(LayoutArgs a) {
     if (tid == 0) a.blk_flags[blockIdx.x] = s_flags;
 }
 
-// Placement pass of the multi-workgroup layout; workgroup b owns tile b.
+// Placement pass of the multi-workgroup layout; workgroup b owns tile b
+// (tiles of J*1024 entries, as in k_layout_local<J>).
+template <int J>
 __global__ __launch_bounds__(kLayoutThreads) void k_layout_place(LayoutArgs a) {
     __shared__ int s_off[kMaxE + 1], s_pex[kMaxE + 1], s_pre[kMaxE];
     __shared__ int2 s_tmp[kLayoutWaves];
@@ -218,8 +221,8 @@ __global__ __launch_bounds__(kLayoutThreads) void k_layout_place(LayoutArgs a) {
     flags |= finish_counts(a, cnt, s_off, s_pex, s_tmp, b == 0, b, a.nblk);
     // tile b's entries: tile rank -> row
 #pragma unroll
-    for (int j = 0; j < kMultiJ; ++j) {
-        const int i = b * kMultiTile + j * kLayoutThreads + tid;
+    for (int j = 0; j < J; ++j) {
+        const int i = b * kLayoutThreads * J + j * kLayoutThreads + tid;
         if (i >= a.N) break;
         const int e = a.idx[i];
         if (e < 0 || e >= a.E) continue;  // already -1
@@ -245,30 +248,36 @@ hipError_t launch_fused(const LayoutArgs &a, size_t lds, hipStream_t s) {
 }  // namespace
 
 size_t layout_workspace_bytes(int64_t N, int E) {
-    if (N <= static_cast<int64_t>(kLayoutThreads) * kFusedMaxJ) return 0;
-    const int64_t nblk = (N + kMultiTile - 1) / kMultiTile;
+    if (N <= kSingleMaxN) return 0;
+    const int64_t tile = static_cast<int64_t>(kLayoutThreads) * multi_tile_j(N);
+    const int64_t nblk = (N + tile - 1) / tile;
     const size_t bytes = static_cast<size_t>(nblk) * E * sizeof(int32_t) + static_cast<size_t>(nblk) * sizeof(int32_t);
     return (bytes + 255) / 256 * 256;
 }
 
-hipError_t launch_layout(const LayoutArgs &a_in, hipStream_t s) {
-    LayoutArgs a = a_in;
-    const size_t lds = static_cast<size_t>(kLayoutWaves) * a.E * sizeof(unsigned short);
-    if (a.N <= kLayoutThreads * kFusedMaxJ) {
-        const int per_lane = (a.N + kLayoutThreads - 1) / kLayoutThreads;
-        if (per_lane <= 1) return launch_fused<1>(a, lds, s);
-        if (per_lane <= 2) return launch_fused<2>(a, lds, s);
-        if (per_lane <= 4) return launch_fused<4>(a, lds, s);
-        if (per_lane <= 8) return launch_fused<8>(a, lds, s);
-        return launch_fused<16>(a, lds, s);
-    }
-    a.nblk = (a.N + kMultiTile - 1) / kMultiTile;
+template <int J>
+hipError_t launch_multi(LayoutArgs a, size_t lds, hipStream_t s) {
+    const int tile = kLayoutThreads * J;
+    a.nblk = (a.N + tile - 1) / tile;
     a.blk_flags = a.blk_hist + static_cast<size_t>(a.nblk) * a.E;
-    hipLaunchKernelGGL(k_layout_local<kMultiJ>, dim3(a.nblk), dim3(kLayoutThreads), lds, s, a);
-    hipError_t err = hipGetLastError();
+    hipLaunchKernelGGL(k_layout_local<J>, dim3(a.nblk), dim3(kLayoutThreads), lds, s, a);
+    const hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    hipLaunchKernelGGL(k_layout_place, dim3(a.nblk), dim3(kLayoutThreads), 0, s, a);
+    hipLaunchKernelGGL(k_layout_place<J>, dim3(a.nblk), dim3(kLayoutThreads), 0, s, a);
     return hipGetLastError();
+}
+
+hipError_t launch_layout(const LayoutArgs &a, hipStream_t s) {
+    const size_t lds = static_cast<size_t>(kLayoutWaves) * a.E * sizeof(unsigned short);
+    if (a.N <= kSingleMaxN) {
+        if (a.N <= kLayoutThreads) return launch_fused<1>(a, lds, s);
+        return launch_fused<2>(a, lds, s);
+    }
+    switch (multi_tile_j(a.N)) {
+        case 1: return launch_multi<1>(a, lds, s);
+        case 2: return launch_multi<2>(a, lds, s);
+        default: return launch_multi<4>(a, lds, s);
+    }
 }
 
 }  // namespace moe
