@@ -243,6 +243,21 @@ def decode_numbers(moe, dcfg, dev, iters: int):
                        "R": dcfg.R, "fp8": dcfg.fp8, "capacity": dcfg.pad_rows}}
 
 
+def cu_budget_numbers(moe, run, counts, steps: int = 10):
+    """Dispatch + combine GB/s when the step runs on a stream limited to n CUs."""
+    import torch
+    out = {}
+    _, db, cb = run.bytes()
+    for n in counts:
+        with moe.CULimitedStream(n) as cs:
+            with torch.cuda.stream(cs.stream):
+                t = time_steps(run, steps, 3)
+            torch.cuda.synchronize()
+        out[str(n)] = {"dispatch_plus_combine_gbps": round((db + cb) / ((t["dispatch_ms"] + t["combine_ms"]) * 1e-3) / 1e9, 1),
+                       "step_us": round(t["step_ms"] * 1e3, 1)}
+    return out
+
+
 def cpu_baseline(cfg, budget_s: float = 12.0):
     """The CPU oracle (single-threaded C) on the same workload: layout, dispatch
     and combine of full batches, repeated until ~budget_s of work."""
@@ -293,6 +308,8 @@ def main(argv=None):
     ap.add_argument("--decode-iters", type=int, default=500)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--cu-budgets", default="32,64,128,256",
+                    help="comma-separated CU counts for the CU-limited-stream sweep ('' to skip)")
     ap.add_argument("--calib-copy", action="store_true")
     ap.add_argument("--only-decode", action="store_true",
                     help="time only the decode call (S=128) and print its JSON object")
@@ -341,6 +358,8 @@ def main(argv=None):
              "bytes": {"layout": lb, "dispatch": db, "combine": cb}, "wall_s_timed": round(t["wall_s"], 3)}
 
     decode = None if args.no_decode else decode_numbers(moe, CONFIGS["decode"], dev, args.decode_iters)
+    budgets = [int(x) for x in args.cu_budgets.split(",") if x.strip()]
+    cu_budget = cu_budget_numbers(moe, run, budgets) if budgets else None
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -354,6 +373,7 @@ def main(argv=None):
                    "fp8_dispatch": cfg.fp8, "routing": cfg.routing, "pad_mode": cfg.pad_mode,
                    "pad_rows": cfg.pad_rows, "shared": cfg.shared, "parallelism": "ep8 simulated on 1 GPU"},
         "roofline": roofline, "cpu_baseline": cpu, "kernels": extra, "decode": decode,
+        "cu_budget": cu_budget,
     }
     print(json.dumps(line), flush=True)
 

@@ -23,7 +23,8 @@ MOE_PAD_NONE, MOE_PAD_MULTIPLE, MOE_PAD_CAPACITY = 0, 1, 2
 MOE_FLAG_BAD_EXPERT, MOE_FLAG_CAPACITY = 1, 2
 
 EXPORTED = ("moe_max_recv_rows", "moe_layout_workspace_bytes", "moe_layout", "moe_dispatch",
-            "moe_layout_dispatch", "moe_combine", "moe_status_str")
+            "moe_layout_dispatch", "moe_combine", "moe_stream_create_cu_limited", "moe_stream_destroy",
+            "moe_status_str")
 
 
 class MoeError(RuntimeError):
@@ -63,6 +64,10 @@ def _load():
     L.moe_layout_dispatch.restype = ctypes.c_int
     L.moe_combine.argtypes = [D, B, P, ctypes.c_int32, P, P, P, P]
     L.moe_combine.restype = ctypes.c_int
+    L.moe_stream_create_cu_limited.argtypes = [ctypes.c_int32, ctypes.POINTER(ctypes.c_void_p)]
+    L.moe_stream_create_cu_limited.restype = ctypes.c_int
+    L.moe_stream_destroy.argtypes = [P]
+    L.moe_stream_destroy.restype = ctypes.c_int
     L.moe_status_str.argtypes = [ctypes.c_int32]
     L.moe_status_str.restype = ctypes.c_char_p
     return L
@@ -151,6 +156,32 @@ def moe_layout_workspace_bytes(desc: LayoutDesc) -> int:
 
 def moe_status_str(status: int) -> str:
     return _lib.moe_status_str(int(status)).decode()
+
+
+class CULimitedStream:
+    """A HIP stream whose kernels run on at most `num_cus` CUs
+    (moe_stream_create_cu_limited), usable as a torch stream."""
+
+    def __init__(self, num_cus: int, device="cuda"):
+        handle = ctypes.c_void_p()
+        rc = _lib.moe_stream_create_cu_limited(int(num_cus), ctypes.byref(handle))
+        if rc != MOE_OK:
+            raise MoeError(rc, "moe_stream_create_cu_limited")
+        self.num_cus = num_cus
+        self.handle = handle.value
+        self.stream = torch.cuda.ExternalStream(self.handle, device=torch.device(device))
+
+    def close(self):
+        if self.handle:
+            torch.cuda.synchronize()
+            _lib.moe_stream_destroy(ctypes.c_void_p(self.handle))
+            self.handle = None
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()
 
 
 def alloc_layout(desc: LayoutDesc, device) -> Layout:

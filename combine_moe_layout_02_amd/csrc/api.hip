@@ -1,7 +1,10 @@
 // C ABI front end of libmoe_ep.so: argument checks, launch-shape choice, and
 // status codes.  Declarations and the meaning of every argument are in
 // include/moe_ep.h.  Nothing here allocates, frees or synchronises.
+#include <hip/hip_ext.h>
 #include <stdint.h>
+
+#include <vector>
 
 #include "moe_ep.h"
 #include "moe_kernels.h"
@@ -188,6 +191,33 @@ moe_status moe_combine(const moe_layout_desc *desc, const moe_layout_bufs *layou
     a.shared = shared_out;
     a.out = out;
     return moe::launch_combine(a, static_cast<hipStream_t>(stream)) == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+moe_status moe_stream_create_cu_limited(int32_t num_cus, void **stream_out) {
+    if (stream_out == nullptr) return MOE_ERR_NULL;
+    int dev = 0, xcc = 1;
+    hipDeviceProp_t prop;
+    if (hipGetDevice(&dev) != hipSuccess || hipGetDeviceProperties(&prop, dev) != hipSuccess) return MOE_ERR_HIP;
+    if (hipDeviceGetAttribute(&xcc, hipDeviceAttributeNumberOfXccs, dev) != hipSuccess || xcc < 1) xcc = 1;
+    const int total = prop.multiProcessorCount;
+    // Bit i of the queue CU mask selects a CU of XCD i % xcc, so the first
+    // num_cus bits give every XCD num_cus / xcc CUs; a mask that leaves an XCD
+    // without CUs is refused by the runtime.
+    if (num_cus < 1 || num_cus > total || num_cus % xcc != 0) return MOE_ERR_SHAPE;
+    std::vector<uint32_t> mask((total + 31) / 32, 0u);
+    for (int i = 0; i < num_cus; ++i) mask[i / 32] |= 1u << (i % 32);
+    hipStream_t s = nullptr;
+    if (hipExtStreamCreateWithCUMask(&s, static_cast<uint32_t>(mask.size()), mask.data()) != hipSuccess) {
+        (void)hipGetLastError();
+        return MOE_ERR_HIP;
+    }
+    *stream_out = s;
+    return MOE_OK;
+}
+
+moe_status moe_stream_destroy(void *stream) {
+    if (stream == nullptr) return MOE_ERR_NULL;
+    return hipStreamDestroy(static_cast<hipStream_t>(stream)) == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 
 const char *moe_status_str(int32_t status) {

@@ -173,6 +173,19 @@ moe_status moe_combine(const moe_layout_desc *desc, const moe_layout_bufs *layou
                        const void *expert_out, int32_t H, const float *w,
                        const void *shared_out, void *out, void *stream);
 
+/* CU budget for overlap: a new stream whose kernels may run only on
+ * `num_cus` compute units, num_cus / (number of XCDs) on every XCD (default
+ * priority).  Launching layout / dispatch / combine on it leaves
+ * the other CUs to concurrent work, the AMD form of DeepEP's control of the
+ * number of SMs its kernels occupy (DeepEP analysis, feature list and the
+ * "normal kernels" paragraph; MoonEP basic usage, num_sms=32).  Results do not
+ * depend on the budget.  Host call: touches the HIP runtime of the current
+ * device, allocates the stream; release it with moe_stream_destroy.
+ * MOE_ERR_SHAPE if num_cus is outside [1, CU count] or not a multiple of the
+ * XCD count (8 on MI355X). */
+moe_status moe_stream_create_cu_limited(int32_t num_cus, void **stream_out);
+moe_status moe_stream_destroy(void *stream);
+
 /* Static string naming a moe_status value. */
 const char *moe_status_str(int32_t status);
 

@@ -420,3 +420,32 @@ def test_layout_dispatch(moe, case):
         assert np.all(got[~valid] == POISON_BF16)
     assert np.array_equal(recv_w.cpu().numpy()[valid].view(np.uint32), rw[valid].view(np.uint32))
     assert np.all(np.isnan(recv_w.cpu().numpy()[~valid]))
+
+
+def test_cu_limited_stream(moe):
+    """Layout, dispatch and combine on a stream limited to 32 CUs give the same
+    bits as on the default stream."""
+    cfg = CONFIGS["prefill"]
+    w = make_workload(cfg)
+    say("case cu-limited stream prefill")
+    buf = moe.Buffer(cfg.S, cfg.H, cfg.K, cfg.E, cfg.R, fp8=True, device=DEV)
+    idx = torch.from_numpy(w.topk_idx).to(DEV)
+    hid = dev_bf16(w.hidden, DEV)
+    tw = torch.from_numpy(w.topk_w).to(DEV)
+    y = torch.randn((buf.rows, cfg.H), device=DEV).to(torch.bfloat16)
+    torch.cuda.synchronize()
+
+    def run():
+        buf.layout_call(idx)
+        buf.dispatch_call(hid, idx, tw)
+        buf.combine_call(y, tw)
+        return [t.clone() for t in (buf.layout.pos, buf.layout.src, buf.recv, buf.recv_scales, buf.out)]
+
+    want = run()
+    torch.cuda.synchronize()
+    with moe.CULimitedStream(32, DEV) as cs:
+        with torch.cuda.stream(cs.stream):
+            got = run()
+        torch.cuda.synchronize()
+    for a, b in zip(got, want):
+        assert torch.equal(a, b)
