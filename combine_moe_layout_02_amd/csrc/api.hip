@@ -100,7 +100,9 @@ moe_status prepare_dispatch(const moe_layout_desc *desc, const void *hidden, int
                             int32_t fp8, void *recv, float *recv_scales, float *recv_w, moe::DispatchArgs &a) {
     if (!desc_ok(desc) || max_rows(desc) < 0 || H < 8 || H % 8 != 0) return MOE_ERR_SHAPE;
     if (fp8 && H % 128 != 0) return MOE_ERR_SHAPE;
-    if ((H / (fp8 ? 16 : 8) + moe::kWave - 1) / moe::kWave > 65535) return MOE_ERR_SHAPE;  // grid.y
+    // one single-wave workgroup per (token, 512- or 1024-channel chunk)
+    if (static_cast<int64_t>(desc->S) * ((H / (fp8 ? 16 : 8) + moe::kWave - 1) / moe::kWave) > INT32_MAX)
+        return MOE_ERR_SHAPE;
     if (desc->S > 0 && (hidden == nullptr || recv == nullptr)) return MOE_ERR_NULL;
     if (desc->S > 0 && fp8 && recv_scales == nullptr) return MOE_ERR_NULL;
     if (!aligned(hidden, 16) || !aligned(recv, 16) || !aligned(recv_scales, 4) || !aligned(recv_w, 4) ||

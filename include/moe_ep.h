@@ -49,8 +49,8 @@
  *     Calls on one stream run in order; calls on different streams that share
  *     output buffers race.
  *   - Limits: 0 <= S, 1 <= K <= 16, 1 <= E <= 1024, R divides E,
- *     S*K and every row count below 2^31; dispatch: H/512 (bf16) or H/1024
- *     (FP8) at most 65535; combine: S*ceil(H/512) below 2^31.
+ *     S*K and every row count below 2^31; dispatch: S*ceil(H/512) (bf16) or
+ *     S*ceil(H/1024) (FP8) below 2^31; combine: S*ceil(H/512) below 2^31.
  */
 #ifndef MOE_EP_H
 #define MOE_EP_H
