@@ -22,7 +22,7 @@ SRC = os.path.join(_HERE, "moe_oracle.c")
 LIB = os.path.join(_HERE, "libmoe_oracle.so")
 
 PAD_NONE, PAD_MULTIPLE, PAD_CAPACITY = 0, 1, 2
-FLAG_BAD_EXPERT, FLAG_CAPACITY = 1, 2
+FLAG_BAD_EXPERT, FLAG_CAPACITY, FLAG_UNBALANCED = 1, 2, 4
 OK, ERR_NULL, ERR_SHAPE = 0, 1, 2
 
 
@@ -67,6 +67,8 @@ def lib():
         L.oracle_dispatch_fp8.restype = i32
         L.oracle_combine.argtypes = [P, i32, i32, i32, P, P, P, P]
         L.oracle_combine.restype = i32
+        L.oracle_layout_balanced.argtypes = [P] + [i32] * 5 + [P] * 9
+        L.oracle_layout_balanced.restype = i32
         L.oracle_bf16_from_f32_n.argtypes = [P, i64, P]
         L.oracle_bf16_from_f32_n.restype = None
         L.oracle_e4m3_from_f32_n.argtypes = [P, i64, P]
@@ -160,6 +162,39 @@ def layout(topk_idx: np.ndarray, E: int, R: int, pad_mode: int = PAD_NONE, pad_r
     if rc != OK:
         raise ValueError(f"oracle_layout failed with {rc}")
     return Layout(tpe, tpr, eoff, roff, pos, src, status)
+
+
+class BalancedLayout(Layout):
+    def __init__(self, seg_offset, slot_expert, **kw):
+        super().__init__(**kw)
+        self.seg_offset = seg_offset
+        self.slot_expert = slot_expert
+
+    def as_dict(self):
+        d = super().as_dict()
+        d.update(seg_offset=self.seg_offset, slot_expert=self.slot_expert)
+        return d
+
+
+def layout_balanced(topk_idx: np.ndarray, E: int, R: int, B: int) -> BalancedLayout:
+    """Balanced layout with B redundant-expert slots per rank (see moe_oracle.c)."""
+    idx = _c(topk_idx, np.int32)
+    S, K = idx.shape
+    if max_recv_rows(S, K, E, R) < 0 or not 0 <= B <= 64:
+        raise ValueError("bad layout shape")
+    epr = E // R
+    out = dict(tokens_per_expert=np.zeros(E, np.int32), tokens_per_rank=np.zeros(R, np.int32),
+               expert_offset=np.zeros(E + 1, np.int32), rank_offset=np.zeros(R + 1, np.int32),
+               pos=np.zeros((S, K), np.int32), src=np.zeros(S * K, np.int32), status=np.zeros(1, np.int32))
+    seg = np.zeros(R * (epr + B) + 1, np.int32)
+    slot = np.zeros(R * B, np.int32)
+    rc = lib().oracle_layout_balanced(_p(idx), S, K, E, R, B, _p(out["tokens_per_expert"]),
+                                      _p(out["tokens_per_rank"]), _p(out["expert_offset"]),
+                                      _p(out["rank_offset"]), _p(out["pos"]), _p(out["src"]), _p(seg),
+                                      _p(slot), _p(out["status"]))
+    if rc != OK:
+        raise ValueError(f"oracle_layout_balanced failed with {rc}")
+    return BalancedLayout(seg, slot, **out)
 
 
 # ---- dispatch / combine -----------------------------------------------------

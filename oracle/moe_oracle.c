@@ -333,3 +333,151 @@ void oracle_dequant_identity(const uint8_t *codes, const float *scales, int64_t 
             y[r * H + c] = oracle_bf16_from_f32(v);
         }
 }
+
+/* ------------------------------------------------------------------------ */
+/* Balanced layout (redundant expert slots)                                   */
+/* ------------------------------------------------------------------------ */
+/* Every rank receives the same number of rows however skewed the routing:
+ * ranks whose own experts hold more entries than their quota hand the surplus
+ * to replicas of those experts placed in free slots of ranks below their quota
+ * (MoonEP article, section 1 "perfect balance": each rank receives exactly
+ * S*K rows through a few redundant experts planned online; section 3, Fig. 3:
+ * each rank holds its local experts followed by B prefetch slots).  The pages
+ * do not give the planning rule; this is the plain greedy reading:
+ *   quota q[r] = N/R, plus one for the first N%R ranks (N = valid entries);
+ *   source ranks in ascending order; inside a rank its experts by count,
+ *   largest first (ties: lower id); each expert sheds what its rank still has
+ *   to shed, at most all its entries;
+ *   each shed amount goes to the lowest destination rank that still has room
+ *   (below its quota) and a free slot, as much as that room allows, then the
+ *   next destination; each (expert, destination) piece takes one slot;
+ *   if no destination is left the rest stays home and the layout is flagged.
+ * Entries of an expert keep their t*K+k order: the first ones stay home, the
+ * following ones fill the expert's replicas in the order they were created.
+ * Rows: rank-major; inside a rank its E/R home segments in expert order, then
+ * its B slot segments in slot order.
+ *   seg_offset  [R*(E/R+B)+1]  first row of each (rank, segment)
+ *   slot_expert [R*B]          expert replicated in each slot, -1 if unused
+ *   expert_offset [E+1]        first row of each expert's home segment; [E] = rows
+ * Other outputs as in oracle_layout (no padding; max rows = S*K). */
+enum { OR_FLAG_UNBALANCED = 4 };
+
+int oracle_layout_balanced(const int32_t *topk_idx, int S, int K, int E, int R, int B,
+                           int32_t *tokens_per_expert, int32_t *tokens_per_rank,
+                           int32_t *expert_offset, int32_t *rank_offset, int32_t *pos,
+                           int32_t *src, int32_t *seg_offset, int32_t *slot_expert,
+                           int32_t *status) {
+    if (!shape_ok(S, K, E, R, OR_PAD_NONE, 0) || B < 0 || B > 64) return OR_ERR_SHAPE;
+    const int64_t n = (int64_t)S * K;
+    const int epr = E / R, nseg = epr + B;
+    int32_t flags = 0;
+
+    int64_t *count = (int64_t *)calloc((size_t)E, sizeof(int64_t));
+    for (int64_t i = 0; i < n; ++i) {
+        int32_t e = topk_idx[i];
+        if (e < 0 || e >= E) { flags |= OR_FLAG_BAD_EXPERT; continue; }
+        count[e] += 1;
+    }
+    int64_t valid = 0;
+    for (int e = 0; e < E; ++e) valid += count[e];
+
+    /* quotas and deficits */
+    int64_t *room = (int64_t *)calloc((size_t)R, sizeof(int64_t));   /* quota - load, may be < 0 */
+    for (int r = 0; r < R; ++r) {
+        int64_t quota = valid / R + (r < valid % R ? 1 : 0);
+        int64_t load = 0;
+        for (int j = 0; j < epr; ++j) load += count[r * epr + j];
+        room[r] = quota - load;
+    }
+
+    /* replicas: expert, destination rank, slot, number of entries */
+    int max_rep = R * B;
+    int *rep_e = (int *)malloc(sizeof(int) * (size_t)(max_rep + 1));
+    int *rep_r = (int *)malloc(sizeof(int) * (size_t)(max_rep + 1));
+    int *rep_s = (int *)malloc(sizeof(int) * (size_t)(max_rep + 1));
+    int64_t *rep_n = (int64_t *)malloc(sizeof(int64_t) * (size_t)(max_rep + 1));
+    int nrep = 0;
+    int *slots_used = (int *)calloc((size_t)R, sizeof(int));
+    int64_t *home = (int64_t *)malloc(sizeof(int64_t) * (size_t)E);
+    for (int e = 0; e < E; ++e) home[e] = count[e];
+    int *order = (int *)malloc(sizeof(int) * (size_t)epr);
+
+    for (int r = 0; r < R; ++r) {
+        int64_t surplus = -room[r];
+        if (surplus <= 0) continue;
+        /* this rank's experts, largest count first, ties by lower id (insertion sort) */
+        for (int j = 0; j < epr; ++j) {
+            int e = r * epr + j, at = j;
+            while (at > 0 && count[order[at - 1]] < count[e]) { order[at] = order[at - 1]; --at; }
+            order[at] = e;
+        }
+        for (int j = 0; j < epr && surplus > 0; ++j) {
+            int e = order[j];
+            int64_t shed = home[e] < surplus ? home[e] : surplus;
+            while (shed > 0) {
+                int d = -1;
+                for (int cand = 0; cand < R; ++cand)
+                    if (room[cand] > 0 && slots_used[cand] < B) { d = cand; break; }
+                if (d < 0) { flags |= OR_FLAG_UNBALANCED; goto planned; }
+                int64_t take = shed < room[d] ? shed : room[d];
+                rep_e[nrep] = e; rep_r[nrep] = d; rep_s[nrep] = slots_used[d]; rep_n[nrep] = take;
+                nrep += 1;
+                slots_used[d] += 1;
+                room[d] -= take;
+                home[e] -= take;
+                shed -= take;
+                surplus -= take;
+                room[r] += take;
+            }
+        }
+    }
+planned:;
+    /* segment sizes, scan */
+    int64_t *seg = (int64_t *)calloc((size_t)R * nseg, sizeof(int64_t));
+    for (int e = 0; e < E; ++e) seg[(int64_t)(e / epr) * nseg + (e % epr)] = home[e];
+    for (int i = 0; i < R * B; ++i) slot_expert[i] = -1;
+    for (int q = 0; q < nrep; ++q) {
+        seg[(int64_t)rep_r[q] * nseg + epr + rep_s[q]] = rep_n[q];
+        slot_expert[rep_r[q] * B + rep_s[q]] = rep_e[q];
+    }
+    int64_t run = 0;
+    for (int64_t g = 0; g < (int64_t)R * nseg; ++g) { seg_offset[g] = (int32_t)run; run += seg[g]; }
+    seg_offset[(int64_t)R * nseg] = (int32_t)run;
+    for (int r = 0; r < R; ++r) {
+        rank_offset[r] = seg_offset[(int64_t)r * nseg];
+        tokens_per_rank[r] = seg_offset[(int64_t)(r + 1) * nseg] - seg_offset[(int64_t)r * nseg];
+    }
+    rank_offset[R] = (int32_t)run;
+    for (int e = 0; e < E; ++e) {
+        tokens_per_expert[e] = (int32_t)count[e];
+        expert_offset[e] = seg_offset[(int64_t)(e / epr) * nseg + (e % epr)];
+    }
+    expert_offset[E] = (int32_t)run;
+
+    /* place entries: per expert, the first home[e] stay, the rest fill its replicas in order */
+    for (int64_t row = 0; row < n; ++row) src[row] = -1;
+    int64_t *seen = (int64_t *)calloc((size_t)E, sizeof(int64_t));
+    for (int64_t i = 0; i < n; ++i) {
+        int32_t e = topk_idx[i];
+        if (e < 0 || e >= E) { pos[i] = -1; continue; }
+        int64_t k = seen[e]++;
+        int64_t row;
+        if (k < home[e]) {
+            row = expert_offset[e] + k;
+        } else {
+            k -= home[e];
+            row = -1;
+            for (int q = 0; q < nrep && row < 0; ++q) {
+                if (rep_e[q] != e) continue;
+                if (k < rep_n[q]) row = seg_offset[(int64_t)rep_r[q] * nseg + epr + rep_s[q]] + k;
+                else k -= rep_n[q];
+            }
+        }
+        pos[i] = (int32_t)row;
+        src[row] = (int32_t)i;
+    }
+    status[0] |= flags;
+    free(count); free(room); free(rep_e); free(rep_r); free(rep_s); free(rep_n); free(slots_used);
+    free(home); free(order); free(seg); free(seen);
+    return OR_OK;
+}

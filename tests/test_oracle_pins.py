@@ -505,3 +505,149 @@ def test_generator_properties():
     w4 = make_workload(c4, with_hidden=False)
     assert abs(maxvio(w4.topk_idx, c4.E) - 20.0) <= 0.5
     assert int(np.bincount(w4.topk_idx.reshape(-1)).argmax()) == 0   # hottest expert is 0
+
+
+# ---------------------------------------------------------------------------
+# balanced layout (redundant expert slots)
+# ---------------------------------------------------------------------------
+
+
+def test_balanced_hand_example():
+    """Worked by hand: E=4 experts on R=2 ranks, B=1 slot, counts [5,1,1,1],
+    N=8 so each rank's quota is 4.  Rank 0 holds 6 (surplus 2), rank 1 holds 2.
+    Expert 0 (rank 0's largest) sheds 2 entries into rank 1's slot 0.  Its
+    entries are t = 0,1,3,5,7: the first three stay home (rows 0..2), t=5 and 7
+    go to the replica (rows 6, 7).  Rows: rank 0 = [e0 x3, e1], rank 1 = [e2,
+    e3, slot0: e0 x2]."""
+    idx = np.array([[0], [0], [1], [0], [2], [0], [3], [0]], np.int32)
+    lo = oracle.layout_balanced(idx, 4, 2, 1)
+    assert lo.tokens_per_rank.tolist() == [4, 4]
+    assert lo.seg_offset.tolist() == [0, 3, 4, 4, 5, 6, 8]
+    assert lo.slot_expert.tolist() == [-1, 0]
+    assert lo.pos.reshape(-1).tolist() == [0, 1, 3, 2, 4, 6, 5, 7]
+    assert lo.expert_offset.tolist() == [0, 3, 4, 5, 8]
+    assert int(lo.status[0]) == 0
+
+
+def test_balanced_hand_example_two_destinations():
+    """E=4, R=4 (one expert per rank), B=2, counts [9,1,1,1] (N=12, quota 3):
+    expert 0 sheds 6: rank 1 takes 2, rank 2 takes 2, rank 3 takes 2 (lowest
+    destination first, each as much as its room).  Not enough slots with B=0:
+    nothing moves and the layout is flagged."""
+    idx = np.array([0] * 9 + [1, 2, 3], np.int32).reshape(12, 1)
+    lo = oracle.layout_balanced(idx, 4, 4, 2)
+    assert lo.tokens_per_rank.tolist() == [3, 3, 3, 3]
+    assert lo.slot_expert.tolist() == [-1, -1, 0, -1, 0, -1, 0, -1]
+    # expert 0's entries 0..8: rows 0,1,2 home; 3,4 -> rank1 slot0 (rows 4,5); 5,6 -> rank2; 7,8 -> rank3
+    assert lo.pos.reshape(-1).tolist()[:9] == [0, 1, 2, 4, 5, 7, 8, 10, 11]
+    lo0 = oracle.layout_balanced(idx, 4, 4, 0)
+    assert int(lo0.status[0]) == oracle.FLAG_UNBALANCED
+    assert lo0.pos.reshape(-1).tolist() == oracle.layout(idx, 4, 4).pos.reshape(-1).tolist()
+
+
+def check_balanced(lo, idx, E, R, B):
+    flat = idx.reshape(-1)
+    n = flat.size
+    pos = lo.pos.reshape(-1)
+    ok = (flat >= 0) & (flat < E)
+    valid = int(ok.sum())
+    epr, nseg = E // R, E // R + B
+    # every valid entry exactly once, rows [0, valid) all used
+    assert np.all(pos[~ok] == -1)
+    assert np.all(lo.src[pos[ok]] == np.nonzero(ok)[0])
+    assert sorted(pos[ok].tolist()) == list(range(valid))
+    assert np.all(lo.src[valid:] == -1)
+    seg = np.diff(lo.seg_offset)
+    assert lo.seg_offset[0] == 0 and lo.seg_offset[-1] == valid
+    quota = [valid // R + (1 if r < valid % R else 0) for r in range(R)]
+    cnt = np.bincount(flat[ok], minlength=E)
+    load = [int(cnt[r * epr:(r + 1) * epr].sum()) for r in range(R)]
+    assert lo.tokens_per_expert.tolist() == cnt.tolist()
+    balanced = not (int(lo.status[0]) & oracle.FLAG_UNBALANCED)
+    for r in range(R):
+        rows = int(lo.seg_offset[(r + 1) * nseg] - lo.seg_offset[r * nseg])
+        assert lo.tokens_per_rank[r] == rows
+        assert lo.rank_offset[r] == lo.seg_offset[r * nseg]
+        if balanced:
+            assert rows == quota[r]
+        # a rank above its quota only sheds, a rank below only receives
+        used = [s for s in range(B) if lo.slot_expert[r * B + s] >= 0]
+        assert used == list(range(len(used)))        # slots fill in order
+        if used:
+            assert load[r] < quota[r]
+            assert rows <= quota[r]
+        for s in range(B):
+            e = lo.slot_expert[r * B + s]
+            if e >= 0:
+                assert e // epr != r                  # never a replica on the owner
+                assert seg[r * nseg + epr + s] > 0
+            else:
+                assert seg[r * nseg + epr + s] == 0
+    # each segment holds entries of one expert; per expert the rows follow t*K+k:
+    # home segment first, then replicas in ascending destination rank
+    seg_of_row = np.searchsorted(lo.seg_offset, np.arange(valid), side="right") - 1
+    for e in range(E):
+        ent = np.nonzero(flat == e)[0]
+        rows = pos[ent]
+        segs = seg_of_row[rows]
+        home_seg = (e // epr) * nseg + e % epr
+        order = [home_seg] + [r * nseg + epr + s for r in range(R) for s in range(B)
+                              if lo.slot_expert[r * B + s] == e]
+        expect = np.concatenate([np.arange(lo.seg_offset[g], lo.seg_offset[g + 1]) for g in order])
+        assert rows.tolist() == expect.tolist()
+        assert set(segs.tolist()) <= set(order)
+        # a shed expert: its rank sheds from its largest experts first
+    for r in range(R):
+        experts = list(range(r * epr, (r + 1) * epr))
+        shed = [e for e in experts if lo.expert_offset[e] >= 0 and
+                (lo.seg_offset[(e // epr) * nseg + e % epr + 1] - lo.seg_offset[(e // epr) * nseg + e % epr]) < cnt[e]]
+        by_size = sorted(experts, key=lambda e: (-cnt[e], e))
+        assert shed == sorted(by_size[:len(shed)])     # the shed set is a prefix of the size order
+    if B == 0 or R == 1:
+        assert pos.tolist() == oracle.layout(idx, E, R).pos.reshape(-1).tolist()
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_balanced_random_invariants(seed):
+    rng = np.random.default_rng(500 + seed)
+    R = int(rng.choice([1, 2, 4, 8]))
+    E = R * int(rng.integers(1, 9))
+    S, K = int(rng.integers(0, 200)), int(rng.integers(1, 5))
+    B = int(rng.integers(0, 5))
+    p = rng.random(E) ** 3                       # skewed expert popularity
+    idx = rng.choice(E, size=(S, K), p=p / p.sum()).astype(np.int32)
+    if seed % 3 == 0 and idx.size:
+        idx.reshape(-1)[rng.integers(0, idx.size, 3)] = -1
+    lo = oracle.layout_balanced(idx, E, R, B)
+    check_balanced(lo, idx, E, R, B)
+
+
+@pytest.mark.parametrize("E,R,B", [(4, 2, 1), (4, 4, 1), (6, 3, 2)])
+def test_balanced_exhaustive_tiny(E, R, B):
+    S, K = 5, 1
+    for combo in itertools.product(range(E), repeat=S * K):
+        idx = np.array(combo, np.int32).reshape(S, K)
+        check_balanced(oracle.layout_balanced(idx, E, R, B), idx, E, R, B)
+
+
+def test_balanced_already_even_is_plain_layout():
+    """Loads already at quota: nothing moves, rows equal the plain layout's."""
+    idx = np.tile(np.arange(8, dtype=np.int32), (6, 1))       # every expert 6 entries
+    lo = oracle.layout_balanced(idx, 8, 4, 3)
+    assert np.all(lo.slot_expert == -1)
+    assert lo.pos.tolist() == oracle.layout(idx, 8, 4).pos.tolist()
+
+
+def test_balanced_skew_config():
+    """The skewed workload (maxvio 20, rank 0 holding 4.3x its quota): with 16
+    slots per rank every rank gets exactly S*K/R = 4096 rows; with 8 slots the
+    planner runs out of room on the last destination and flags it."""
+    cfg = CONFIGS["skew"]
+    w = make_workload(cfg, with_hidden=False)
+    lo = oracle.layout_balanced(w.topk_idx, cfg.E, cfg.R, 16)
+    assert int(lo.status[0]) == 0
+    assert lo.tokens_per_rank.tolist() == [cfg.S * cfg.K // cfg.R] * cfg.R
+    check_balanced(lo, w.topk_idx, cfg.E, cfg.R, 16)
+    lo8 = oracle.layout_balanced(w.topk_idx, cfg.E, cfg.R, 8)
+    assert int(lo8.status[0]) == oracle.FLAG_UNBALANCED
+    check_balanced(lo8, w.topk_idx, cfg.E, cfg.R, 8)
