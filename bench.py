@@ -258,6 +258,32 @@ def cu_budget_numbers(moe, run, counts, steps: int = 10):
     return out
 
 
+def balanced_numbers(moe, cfg, dev, slots: int = 16, iters: int = 200):
+    """Balanced layout (redundant-expert slots) on a skewed batch: time per
+    call next to the plain layout, and rows per rank before / after."""
+    import numpy as np
+    import torch
+    from workloads import make_workload
+    w = make_workload(cfg, with_hidden=False)
+    desc = moe.LayoutDesc(cfg.S, cfg.K, cfg.E, cfg.R)
+    idx = torch.from_numpy(w.topk_idx).to(dev)
+    lay = moe.alloc_layout(desc, dev)
+    bal = moe.alloc_balance(desc, slots, dev)
+    moe.moe_layout(desc, idx, lay)
+    torch.cuda.synchronize()
+    plain_rows = lay.tokens_per_rank.cpu().numpy()
+    plain_ms = time_calls(lambda: moe.moe_layout(desc, idx, lay), iters)
+    bal_ms = time_calls(lambda: moe.moe_layout_balanced(desc, slots, idx, lay, bal), iters)
+    rows = lay.tokens_per_rank.cpu().numpy()
+    status = int(lay.status.cpu().numpy()[0])
+    used = int((bal.slot_expert.cpu().numpy()[:cfg.R * slots] >= 0).sum())
+    return {"workload": cfg.name, "slots_per_rank": slots, "balanced_layout_us": round(bal_ms * 1e3, 2),
+            "plain_layout_us": round(plain_ms * 1e3, 2),
+            "rows_per_rank_max_over_mean_plain": round(float(plain_rows.max() / plain_rows.mean()), 3),
+            "rows_per_rank_max_over_mean_balanced": round(float(rows.max() / rows.mean()), 3),
+            "replica_slots_used": used, "unbalanced_flag": bool(status & 4)}
+
+
 def cpu_baseline(cfg, budget_s: float = 12.0):
     """The CPU oracle (single-threaded C) on the same workload: layout, dispatch
     and combine of full batches, repeated until ~budget_s of work."""
@@ -358,6 +384,7 @@ def main(argv=None):
              "bytes": {"layout": lb, "dispatch": db, "combine": cb}, "wall_s_timed": round(t["wall_s"], 3)}
 
     decode = None if args.no_decode else decode_numbers(moe, CONFIGS["decode"], dev, args.decode_iters)
+    balanced = None if args.no_decode else balanced_numbers(moe, CONFIGS["skew"], dev)
     budgets = [int(x) for x in args.cu_budgets.split(",") if x.strip()]
     cu_budget = cu_budget_numbers(moe, run, budgets) if budgets else None
 
@@ -373,7 +400,7 @@ def main(argv=None):
                    "fp8_dispatch": cfg.fp8, "routing": cfg.routing, "pad_mode": cfg.pad_mode,
                    "pad_rows": cfg.pad_rows, "shared": cfg.shared, "parallelism": "ep8 simulated on 1 GPU"},
         "roofline": roofline, "cpu_baseline": cpu, "kernels": extra, "decode": decode,
-        "cu_budget": cu_budget,
+        "cu_budget": cu_budget, "balanced_layout": balanced,
     }
     print(json.dumps(line), flush=True)
 

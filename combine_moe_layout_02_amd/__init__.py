@@ -20,11 +20,11 @@ LIB_PATH = os.path.join(_HERE, "libmoe_ep.so")
 
 MOE_OK, MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_ALIGN, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(6)
 MOE_PAD_NONE, MOE_PAD_MULTIPLE, MOE_PAD_CAPACITY = 0, 1, 2
-MOE_FLAG_BAD_EXPERT, MOE_FLAG_CAPACITY = 1, 2
+MOE_FLAG_BAD_EXPERT, MOE_FLAG_CAPACITY, MOE_FLAG_UNBALANCED = 1, 2, 4
 
 EXPORTED = ("moe_max_recv_rows", "moe_layout_workspace_bytes", "moe_layout", "moe_dispatch",
-            "moe_layout_dispatch", "moe_combine", "moe_stream_create_cu_limited", "moe_stream_destroy",
-            "moe_status_str")
+            "moe_layout_dispatch", "moe_combine", "moe_layout_balanced_workspace_bytes", "moe_layout_balanced",
+            "moe_stream_create_cu_limited", "moe_stream_destroy", "moe_status_str")
 
 
 class MoeError(RuntimeError):
@@ -41,6 +41,10 @@ class moe_layout_desc(ctypes.Structure):
 class moe_layout_bufs(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in ("tokens_per_expert", "tokens_per_rank", "expert_offset",
                                                "rank_offset", "pos", "src", "status")]
+
+
+class moe_balance_bufs(ctypes.Structure):
+    _fields_ = [("seg_offset", ctypes.c_void_p), ("slot_expert", ctypes.c_void_p)]
 
 
 def _load():
@@ -64,6 +68,11 @@ def _load():
     L.moe_layout_dispatch.restype = ctypes.c_int
     L.moe_combine.argtypes = [D, B, P, ctypes.c_int32, P, P, P, P]
     L.moe_combine.restype = ctypes.c_int
+    L.moe_layout_balanced_workspace_bytes.argtypes = [D, ctypes.c_int32]
+    L.moe_layout_balanced_workspace_bytes.restype = ctypes.c_size_t
+    L.moe_layout_balanced.argtypes = [D, ctypes.c_int32, P, B, ctypes.POINTER(moe_balance_bufs), P,
+                                      ctypes.c_size_t, P]
+    L.moe_layout_balanced.restype = ctypes.c_int
     L.moe_stream_create_cu_limited.argtypes = [ctypes.c_int32, ctypes.POINTER(ctypes.c_void_p)]
     L.moe_stream_create_cu_limited.restype = ctypes.c_int
     L.moe_stream_destroy.argtypes = [P]
@@ -244,6 +253,49 @@ def moe_dispatch(desc: LayoutDesc, layout: Layout, hidden: torch.Tensor, topk_id
     if rc != MOE_OK:
         raise MoeError(rc, "moe_dispatch")
     return recv, (recv_scales if fp8 else None), recv_w
+
+
+def moe_layout_balanced_workspace_bytes(desc: LayoutDesc, slots_per_rank: int) -> int:
+    d = desc.c()
+    return int(_lib.moe_layout_balanced_workspace_bytes(ctypes.byref(d), int(slots_per_rank)))
+
+
+@dataclasses.dataclass
+class Balance:
+    """Device outputs of moe_layout_balanced beyond the layout."""
+    seg_offset: torch.Tensor    # [R*(E/R+B)+1] int32
+    slot_expert: torch.Tensor   # [R*B] int32
+    workspace: torch.Tensor     # scratch (uint8)
+
+    def c(self) -> moe_balance_bufs:
+        return moe_balance_bufs(self.seg_offset.data_ptr(), self.slot_expert.data_ptr())
+
+
+def alloc_balance(desc: LayoutDesc, slots_per_rank: int, device) -> Balance:
+    epr = desc.E // desc.R
+    ws = moe_layout_balanced_workspace_bytes(desc, slots_per_rank)
+    return Balance(torch.empty(desc.R * (epr + slots_per_rank) + 1, dtype=torch.int32, device=device),
+                   torch.empty(max(desc.R * slots_per_rank, 1), dtype=torch.int32, device=device),
+                   torch.empty(max(ws, 256), dtype=torch.uint8, device=device))
+
+
+def moe_layout_balanced(desc: LayoutDesc, slots_per_rank: int, topk_idx: torch.Tensor,
+                        layout: Optional[Layout] = None, balance: Optional[Balance] = None, stream=None):
+    """Balanced layout (equal rows per rank through redundant-expert slots).
+    Returns (layout, balance)."""
+    dev = topk_idx.device
+    _check(topk_idx, "topk_idx", torch.int32, (desc.S, desc.K))
+    if layout is None:
+        layout = alloc_layout(desc, dev)
+    if balance is None:
+        balance = alloc_balance(desc, slots_per_rank, dev)
+    d, b, bb = desc.c(), layout.c(), balance.c()
+    rc = _lib.moe_layout_balanced(ctypes.byref(d), int(slots_per_rank), _ptr(topk_idx), ctypes.byref(b),
+                                  ctypes.byref(bb), _ptr(balance.workspace), balance.workspace.numel(),
+                                  _stream(stream, dev))
+    if rc != MOE_OK:
+        raise MoeError(rc, "moe_layout_balanced")
+    return layout, balance
 
 
 def moe_layout_dispatch(desc: LayoutDesc, topk_idx: torch.Tensor, hidden: torch.Tensor, topk_w=None,

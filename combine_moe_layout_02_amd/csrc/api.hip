@@ -58,7 +58,8 @@ namespace {
 
 // Checks shared by moe_layout and moe_layout_dispatch; fills the kernel args.
 moe_status prepare_layout(const moe_layout_desc *desc, const int32_t *topk_idx, const moe_layout_bufs *out,
-                          void *workspace, size_t workspace_bytes, moe::LayoutArgs &a) {
+                          void *workspace, size_t workspace_bytes, moe::LayoutArgs &a,
+                          bool check_workspace = true) {
     if (desc == nullptr || out == nullptr) return MOE_ERR_NULL;
     if (!desc_ok(desc) || max_rows(desc) < 0) return MOE_ERR_SHAPE;
     const int64_t n = static_cast<int64_t>(desc->S) * desc->K;
@@ -72,8 +73,8 @@ moe_status prepare_layout(const moe_layout_desc *desc, const int32_t *topk_idx, 
     for (const void *p : ints)
         if (!aligned(p, 4)) return MOE_ERR_ALIGN;
     const size_t need = moe::layout_workspace_bytes(n, desc->E);
-    if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return MOE_ERR_WORKSPACE;
-    if (need > 0 && !aligned(workspace, 16)) return MOE_ERR_ALIGN;
+    if (check_workspace && need > 0 && (workspace == nullptr || workspace_bytes < need)) return MOE_ERR_WORKSPACE;
+    if (check_workspace && need > 0 && !aligned(workspace, 16)) return MOE_ERR_ALIGN;
     a = moe::LayoutArgs{};
     a.idx = topk_idx;
     a.N = static_cast<int32_t>(n);
@@ -193,6 +194,46 @@ moe_status moe_combine(const moe_layout_desc *desc, const moe_layout_bufs *layou
     a.shared = shared_out;
     a.out = out;
     return moe::launch_combine(a, static_cast<hipStream_t>(stream)) == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+size_t moe_layout_balanced_workspace_bytes(const moe_layout_desc *desc, int32_t slots_per_rank) {
+    if (desc == nullptr || !desc_ok(desc) || slots_per_rank < 0) return 0;
+    return moe::balance_workspace_bytes(static_cast<int64_t>(desc->S) * desc->K, desc->E, desc->R);
+}
+
+moe_status moe_layout_balanced(const moe_layout_desc *desc, int32_t slots_per_rank, const int32_t *topk_idx,
+                               const moe_layout_bufs *out, const moe_balance_bufs *bal, void *workspace,
+                               size_t workspace_bytes, void *stream) {
+    if (desc == nullptr || out == nullptr || bal == nullptr) return MOE_ERR_NULL;
+    if (!desc_ok(desc) || desc->pad_mode != MOE_PAD_NONE || slots_per_rank < 0 ||
+        slots_per_rank > moe::kMaxSlotsPerRank || static_cast<int64_t>(desc->R) * slots_per_rank > moe::kMaxBalanceSlots)
+        return MOE_ERR_SHAPE;
+    moe::LayoutArgs la;
+    // the checks of moe_layout; its own workspace is carved out of ours
+    const moe_status st = prepare_layout(desc, topk_idx, out, nullptr, 0, la, false);
+    if (st != MOE_OK) return st;
+    if (bal->seg_offset == nullptr || (slots_per_rank > 0 && bal->slot_expert == nullptr)) return MOE_ERR_NULL;
+    if (!aligned(bal->seg_offset, 4) || !aligned(bal->slot_expert, 4)) return MOE_ERR_ALIGN;
+    const size_t need = moe::balance_workspace_bytes(la.N, desc->E, desc->R);
+    if (workspace == nullptr || workspace_bytes < need) return MOE_ERR_WORKSPACE;
+    if (!aligned(workspace, 256)) return MOE_ERR_ALIGN;
+    moe::BalanceArgs b{};
+    b.idx = topk_idx;
+    b.N = la.N;
+    b.E = desc->E;
+    b.R = desc->R;
+    b.B = slots_per_rank;
+    b.tpe = out->tokens_per_expert;
+    b.tpr = out->tokens_per_rank;
+    b.eoff = out->expert_offset;
+    b.roff = out->rank_offset;
+    b.pos = out->pos;
+    b.src = out->src;
+    b.status = out->status;
+    b.seg_offset = bal->seg_offset;
+    b.slot_expert = bal->slot_expert;
+    return moe::launch_layout_balanced(la, b, workspace, static_cast<hipStream_t>(stream)) == hipSuccess
+               ? MOE_OK : MOE_ERR_HIP;
 }
 
 moe_status moe_stream_create_cu_limited(int32_t num_cus, void **stream_out) {

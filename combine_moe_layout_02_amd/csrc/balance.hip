@@ -1,0 +1,234 @@
+// Balanced layout: every rank receives the same number of rows, however skewed
+// the routing, by moving the surplus of overloaded ranks into redundant copies
+// of their experts held in per-rank slots (MoonEP article, section 1: perfect
+// balance through a few redundant experts planned online; section 3 and
+// Fig. 3: each rank's local experts followed by B prefetch slots).
+//
+// The pages give the invariant, not the planning rule.  The rule here (the
+// plain greedy reading):
+//   quota q[r] = N/R, plus one for the first N%R ranks (N = valid entries);
+//   overloaded ranks in ascending order shed their surplus from their largest
+//   experts first (ties: lower id), each expert at most all of its entries;
+//   every shed piece goes to the lowest rank still below its quota that has a
+//   free slot, as much as that rank's room allows, then to the next one; each
+//   (expert, destination) piece takes one slot; if no rank is left the rest
+//   stays home and status bit 2 is set.
+// An expert's first entries (t*K+k order) stay home; the following ones fill
+// its replicas in creation order.  Rows are rank-major: the rank's E/R home
+// segments in expert order, then its B slot segments.
+//
+// Implementation: the plain layout is computed first (into workspace); it
+// gives each entry's stable rank inside its expert (pos - expert_offset).
+// k_balance_place then runs on G workgroups; each one rebuilds the plan --
+// counts and loads, the per-rank size order of experts (each thread counts the
+// experts that precede its own), the greedy (one thread; the destination
+// cursor only moves forward, so O(E + R + replicas) steps), segment offsets
+// (workgroup scan) -- and remaps its share of entries.  Workgroup 0 writes the
+// per-expert / per-rank / per-segment outputs.
+#include "moe_kernels.h"
+
+namespace moe {
+namespace {
+
+struct BalanceLds {
+    int cnt[kMaxE];           // entries per expert
+    int home[kMaxE];          // entries that stay on the owner
+    int order[kMaxE];         // experts of each rank, largest first
+    int first_rep[kMaxE];     // first replica of each expert (creation order)
+    int nrep_e[kMaxE];
+    int room[kMaxE];          // quota - current rows, per rank (R <= E)
+    int slots_used[kMaxE];
+    int rep_e[kMaxBalanceSlots];
+    int rep_n[kMaxBalanceSlots];
+    int rep_rs[kMaxBalanceSlots];    // (destination rank << 8) | slot
+    int slot_rep[kMaxBalanceSlots];  // replica held by (rank, slot), -1 if none
+    int seg_off[kMaxE + kMaxBalanceSlots + 1];
+    int2 tmp[kLayoutWaves];
+    int nrep;
+    int flags;
+};
+
+__global__ __launch_bounds__(kLayoutThreads) void k_balance_place(BalanceArgs b) {
+    __shared__ BalanceLds L;
+    const int tid = threadIdx.x;
+    const int E = b.E, R = b.R, B = b.B, epr = E / R, nseg = epr + B, ngrp = R * nseg;
+
+    // counts from the plain layout, loads and quotas
+    for (int e = tid; e < E; e += kLayoutThreads) {
+        L.cnt[e] = b.tpe_std[e];
+        L.home[e] = L.cnt[e];
+        L.first_rep[e] = 0;
+        L.nrep_e[e] = 0;
+    }
+    for (int q = tid; q < R * B; q += kLayoutThreads) L.slot_rep[q] = -1;
+    if (tid == 0) {
+        L.nrep = 0;
+        L.flags = b.status_std[0];
+    }
+    __syncthreads();
+    const int valid = b.eoff_std[E];
+    for (int r = tid; r < R; r += kLayoutThreads) {
+        int load = 0;
+        for (int j = 0; j < epr; ++j) load += L.cnt[r * epr + j];
+        L.room[r] = valid / R + (r < valid % R ? 1 : 0) - load;
+        L.slots_used[r] = 0;
+    }
+    // position of each expert in its rank's size order (count desc, id asc)
+    for (int e = tid; e < E; e += kLayoutThreads) {
+        const int r0 = (e / epr) * epr, c = L.cnt[e];
+        int before = 0;
+        for (int j = r0; j < r0 + epr; ++j) {
+            const int cj = L.cnt[j];
+            before += (cj > c || (cj == c && j < e)) ? 1 : 0;
+        }
+        L.order[r0 + before] = e;
+    }
+    __syncthreads();
+
+    // the greedy plan (one thread)
+    if (tid == 0) {
+        int dst = 0, nrep = 0, flags = L.flags;
+        for (int r = 0; r < R && !(flags & FLAG_UNBALANCED); ++r) {
+            int surplus = -L.room[r];
+            for (int j = 0; j < epr && surplus > 0; ++j) {
+                const int e = L.order[r * epr + j];
+                int shed = L.home[e] < surplus ? L.home[e] : surplus;
+                while (shed > 0) {
+                    while (dst < R && (L.room[dst] <= 0 || L.slots_used[dst] >= B)) ++dst;
+                    if (dst == R) {
+                        flags |= FLAG_UNBALANCED;
+                        break;
+                    }
+                    const int take = shed < L.room[dst] ? shed : L.room[dst];
+                    const int slot = L.slots_used[dst]++;
+                    if (L.nrep_e[e] == 0) L.first_rep[e] = nrep;
+                    L.nrep_e[e] += 1;
+                    L.rep_e[nrep] = e;
+                    L.rep_n[nrep] = take;
+                    L.rep_rs[nrep] = (dst << 8) | slot;
+                    L.slot_rep[dst * B + slot] = nrep;
+                    ++nrep;
+                    L.room[dst] -= take;
+                    L.home[e] -= take;
+                    shed -= take;
+                    surplus -= take;
+                    L.room[r] += take;
+                }
+                if (flags & FLAG_UNBALANCED) break;
+            }
+        }
+        L.nrep = nrep;
+        L.flags = flags;
+    }
+    __syncthreads();
+
+    // segment sizes -> offsets (each thread scans a run of consecutive segments)
+    const int per = (ngrp + kLayoutThreads - 1) / kLayoutThreads;
+    const int g0 = tid * per;
+    auto seg_size = [&](int g) -> int {
+        const int r = g / nseg, j = g % nseg;
+        if (j < epr) return L.home[r * epr + j];
+        const int q = L.slot_rep[r * B + (j - epr)];
+        return q >= 0 ? L.rep_n[q] : 0;
+    };
+    int local = 0;
+    for (int g = g0; g < g0 + per && g < ngrp; ++g) local += seg_size(g);
+    int2 total;
+    const int2 ex = block_exclusive_scan2(make_int2(local, 0), L.tmp, total);
+    int run = ex.x;
+    for (int g = g0; g < g0 + per && g < ngrp; ++g) {
+        L.seg_off[g] = run;
+        run += seg_size(g);
+    }
+    if (tid == 0) L.seg_off[ngrp] = total.x;
+    __syncthreads();
+
+    // count-only outputs (workgroup 0)
+    if (blockIdx.x == 0) {
+        for (int g = tid; g <= ngrp; g += kLayoutThreads) b.seg_offset[g] = L.seg_off[g];
+        for (int e = tid; e < E; e += kLayoutThreads) {
+            b.tpe[e] = L.cnt[e];
+            b.eoff[e] = L.seg_off[(e / epr) * nseg + (e % epr)];
+        }
+        for (int r = tid; r < R; r += kLayoutThreads) {
+            b.roff[r] = L.seg_off[r * nseg];
+            b.tpr[r] = L.seg_off[(r + 1) * nseg] - L.seg_off[r * nseg];
+        }
+        for (int q = tid; q < R * B; q += kLayoutThreads) {
+            const int rep = L.slot_rep[q];
+            b.slot_expert[q] = rep >= 0 ? L.rep_e[rep] : -1;
+        }
+        if (tid == 0) {
+            b.eoff[E] = L.seg_off[ngrp];
+            b.roff[R] = L.seg_off[ngrp];
+            b.status[0] = L.flags;
+        }
+    }
+
+    // this workgroup's entries: stable rank inside the expert -> balanced row
+    const int stride = gridDim.x * kLayoutThreads;
+    for (int i = blockIdx.x * kLayoutThreads + tid; i < b.N; i += stride) {
+        const int e = b.idx[i];
+        int row = -1;
+        if (e >= 0 && e < E) {
+            int k = b.pos_std[i] - b.eoff_std[e];
+            if (k < L.home[e]) {
+                row = L.seg_off[(e / epr) * nseg + (e % epr)] + k;
+            } else {
+                k -= L.home[e];
+                const int q0 = L.first_rep[e], q1 = q0 + L.nrep_e[e];
+                for (int q = q0; q < q1; ++q) {
+                    if (k < L.rep_n[q]) {
+                        const int rs = L.rep_rs[q];
+                        row = L.seg_off[(rs >> 8) * nseg + epr + (rs & 0xFF)] + k;
+                        break;
+                    }
+                    k -= L.rep_n[q];
+                }
+            }
+        }
+        b.pos[i] = row;
+        if (row >= 0) b.src[row] = i;
+    }
+    // rows past the valid ones (only when some ids were out of range)
+    for (int r = L.seg_off[ngrp] + blockIdx.x * kLayoutThreads + tid; r < b.N; r += stride) b.src[r] = -1;
+}
+
+}  // namespace
+
+size_t balance_workspace_bytes(int64_t N, int E, int R) {
+    auto up = [](size_t x) { return (x + 255) / 256 * 256; };
+    return up(static_cast<size_t>(N) * 4) * 2 + up(static_cast<size_t>(E) * 4) + up(static_cast<size_t>(R) * 4) +
+           up(static_cast<size_t>(E + 1) * 4) + up(static_cast<size_t>(R + 1) * 4) + up(4) +
+           layout_workspace_bytes(N, E);
+}
+
+hipError_t launch_layout_balanced(const LayoutArgs &la_in, BalanceArgs b, void *workspace, hipStream_t s) {
+    auto up = [](size_t x) { return (x + 255) / 256 * 256; };
+    char *ws = static_cast<char *>(workspace);
+    const int64_t N = la_in.N;
+    LayoutArgs la = la_in;  // the plain layout, written to workspace
+    la.pos = reinterpret_cast<int32_t *>(ws); ws += up(static_cast<size_t>(N) * 4);
+    la.src = reinterpret_cast<int32_t *>(ws); ws += up(static_cast<size_t>(N) * 4);
+    la.tpe = reinterpret_cast<int32_t *>(ws); ws += up(static_cast<size_t>(la.E) * 4);
+    la.tpr = reinterpret_cast<int32_t *>(ws); ws += up(static_cast<size_t>(la.R) * 4);
+    la.eoff = reinterpret_cast<int32_t *>(ws); ws += up(static_cast<size_t>(la.E + 1) * 4);
+    la.roff = reinterpret_cast<int32_t *>(ws); ws += up(static_cast<size_t>(la.R + 1) * 4);
+    la.status = reinterpret_cast<int32_t *>(ws); ws += up(4);
+    la.blk_hist = reinterpret_cast<int32_t *>(ws);
+    la.pad_mode = PAD_NONE;
+    la.pad_rows = 0;
+    la.max_recv = static_cast<int32_t>(N);
+    hipError_t err = launch_layout(la, s);
+    if (err != hipSuccess) return err;
+    b.pos_std = la.pos;
+    b.tpe_std = la.tpe;
+    b.eoff_std = la.eoff;
+    b.status_std = la.status;
+    const int64_t wgs = (N + kLayoutThreads - 1) / kLayoutThreads;
+    const int grid = static_cast<int>(wgs < 1 ? 1 : (wgs > 256 ? 256 : wgs));
+    hipLaunchKernelGGL(k_balance_place, dim3(grid), dim3(kLayoutThreads), 0, s, b);
+    return hipGetLastError();
+}
+
+}  // namespace moe

@@ -54,7 +54,23 @@ struct CombineArgs {
 constexpr int kFusedDispatchMaxN = 4096;
 constexpr int kFusedDispatchThreads = 256;
 
+// balanced layout: at most this many redundant-expert slots in total (R*B)
+constexpr int kMaxBalanceSlots = 1024;
+constexpr int kMaxSlotsPerRank = 64;
+enum { FLAG_UNBALANCED = 4 };
+
+struct BalanceArgs {
+    const int32_t *idx;
+    int32_t N, E, R, B;
+    const int32_t *pos_std, *tpe_std, *eoff_std, *status_std;  // plain layout (workspace)
+    int32_t *tpe, *tpr, *eoff, *roff, *pos, *src, *status;
+    int32_t *seg_offset;   // [R*(E/R+B)+1]
+    int32_t *slot_expert;  // [R*B]
+};
+
 size_t layout_workspace_bytes(int64_t N, int E);
+size_t balance_workspace_bytes(int64_t N, int E, int R);
+hipError_t launch_layout_balanced(const LayoutArgs &la, BalanceArgs b, void *workspace, hipStream_t stream);
 hipError_t launch_layout_dispatch_small(const LayoutArgs &la, const DispatchArgs &da, bool fp8,
                                         hipStream_t stream);
 hipError_t launch_layout(const LayoutArgs &a, hipStream_t stream);

@@ -173,6 +173,40 @@ moe_status moe_combine(const moe_layout_desc *desc, const moe_layout_bufs *layou
                        const void *expert_out, int32_t H, const float *w,
                        const void *shared_out, void *out, void *stream);
 
+/* Balanced layout: every rank receives the same number of rows (N/R, the
+ * first N%R ranks one more; N = entries with a valid expert) however skewed
+ * the routing, through redundant copies of experts held in per-rank slots --
+ * the perfect-balance scheme of the MoonEP article (section 1: a few
+ * redundant experts planned online; section 3, Fig. 3: each rank's local
+ * experts followed by B prefetch slots).  The planning rule (the pages give
+ * none): overloaded ranks in ascending order shed their surplus from their
+ * largest experts first (ties: lower id); each piece goes to the lowest rank
+ * still below its quota that has a free slot, as much as its room allows;
+ * each (expert, destination) piece takes one slot; an expert's first entries
+ * (t*K+k order) stay home, later ones fill its replicas in creation order.
+ * If slots run out the rest stays home and status bit 4 is set.
+ *   desc       pad_mode must be MOE_PAD_NONE; rows used <= S*K (src has S*K).
+ *   slots_per_rank  B, 0..64, R*B <= 1024.
+ *   out        as moe_layout; expert_offset[e] = first row of e's home segment,
+ *              expert_offset[E] = rows used; tokens_per_rank = rows per rank.
+ *   bal        seg_offset [R*(E/R+B)+1]: first row of each (rank, segment),
+ *              segments per rank = its E/R experts then its B slots;
+ *              slot_expert [R*B]: expert copied in each slot, -1 if unused
+ *              (the weights a rank must hold in that slot).
+ *   workspace  at least moe_layout_balanced_workspace_bytes, 256-byte aligned.
+ * pos/src are ordinary maps, so moe_dispatch and moe_combine take this
+ * layout unchanged. */
+enum { MOE_FLAG_UNBALANCED = 4 };
+typedef struct {
+    int32_t *seg_offset;  /* [R*(E/R+B)+1] */
+    int32_t *slot_expert; /* [R*B] */
+} moe_balance_bufs;
+size_t moe_layout_balanced_workspace_bytes(const moe_layout_desc *desc, int32_t slots_per_rank);
+moe_status moe_layout_balanced(const moe_layout_desc *desc, int32_t slots_per_rank,
+                               const int32_t *topk_idx, const moe_layout_bufs *out,
+                               const moe_balance_bufs *bal, void *workspace, size_t workspace_bytes,
+                               void *stream);
+
 /* CU budget for overlap: a new stream whose kernels may run only on
  * `num_cus` compute units, num_cus / (number of XCDs) on every XCD (default
  * priority).  Launching layout / dispatch / combine on it leaves

@@ -449,3 +449,67 @@ def test_cu_limited_stream(moe):
         torch.cuda.synchronize()
     for a, b in zip(got, want):
         assert torch.equal(a, b)
+
+
+BAL = [
+    # name, S, K, E, R, B, routing
+    ("skew-B16", 4096, 8, 256, 8, 16, "skew"),
+    ("skew-B8-unbalanced", 4096, 8, 256, 8, 8, "skew"),
+    ("random-small", 300, 4, 32, 4, 3, "pow"),
+    ("random-bad-ids", 1000, 6, 64, 8, 4, "bad"),
+    ("one-rank", 500, 2, 16, 1, 4, "pow"),
+    ("no-slots", 700, 3, 24, 4, 0, "pow"),
+    ("E1024-R8-B64", 2000, 8, 1024, 8, 64, "pow"),
+    ("empty", 0, 4, 16, 4, 2, "pow"),
+]
+
+
+@pytest.mark.parametrize("case", BAL, ids=[c[0] for c in BAL])
+def test_layout_balanced(moe, case):
+    """Balanced layout (redundant-expert slots) against the oracle, every output
+    bit for bit; then bf16 dispatch and combine through the balanced maps."""
+    name, S, K, E, R, B, routing = case
+    seed = 8000 + BAL.index(case)
+    rng = np.random.default_rng(seed)
+    if routing == "skew":
+        w = make_workload(CONFIGS["skew"])
+        idx, hidden, tw = w.topk_idx, w.hidden, w.topk_w
+        H = 1024
+        hidden = np.ascontiguousarray(hidden[:, :H])
+    else:
+        H = 64
+        p = rng.random(E) ** 3
+        idx = rng.choice(E, size=(S, K), p=p / p.sum()).astype(np.int32)
+        if routing == "bad" and idx.size:
+            idx.reshape(-1)[rng.integers(0, idx.size, 20)] = -1
+        hidden = make_workload(_case(name, max(S, 1), H, E, 1, 1), seed=seed).hidden[:S]
+        tw = rng.random((S, K)).astype(np.float32)
+    say(f"case balanced {name}: S={S} K={K} E={E} R={R} B={B}")
+    desc = moe.LayoutDesc(S, K, E, R)
+    lay, bal = moe.moe_layout_balanced(desc, B, torch.from_numpy(np.ascontiguousarray(idx)).to(DEV))
+    torch.cuda.synchronize()
+    ref = oracle.layout_balanced(idx, E, R, B)
+    for k in ("tokens_per_expert", "tokens_per_rank", "expert_offset", "rank_offset", "pos", "src", "status"):
+        want = getattr(ref, k)
+        got = getattr(lay, k).cpu().numpy().reshape(want.shape)
+        assert np.array_equal(got, want), k
+    assert np.array_equal(bal.seg_offset.cpu().numpy(), ref.seg_offset)
+    if B > 0:
+        assert np.array_equal(bal.slot_expert.cpu().numpy()[:R * B], ref.slot_expert)
+    if routing == "skew":
+        assert (int(ref.status[0]) & oracle.FLAG_UNBALANCED) == (0 if B == 16 else oracle.FLAG_UNBALANCED)
+    if S == 0:
+        return
+    # dispatch and combine take the balanced maps unchanged
+    rows = moe.moe_max_recv_rows(desc)
+    valid = ref.src >= 0
+    recv = torch.full((rows, H), POISON_BF16, dtype=torch.int16, device=DEV).view(torch.bfloat16)
+    tw_d = torch.from_numpy(np.ascontiguousarray(tw)).to(DEV)
+    moe.moe_dispatch(desc, lay, dev_bf16(hidden, DEV), topk_w=tw_d, recv=recv)
+    torch.cuda.synchronize()
+    rb, _ = oracle.dispatch_bf16(hidden, ref.pos, rows, tw)
+    assert np.array_equal(host_bits(recv)[valid], rb[valid])
+    y = random_expert_out_bits(seed, rows, H, row_mask=valid, poison=POISON_BF16)
+    out = moe.moe_combine(desc, lay, dev_bf16(y, DEV), tw_d)
+    torch.cuda.synchronize()
+    assert_combine_matches(host_bits(out), oracle.combine(y, ref.pos, tw), "balanced combine")
