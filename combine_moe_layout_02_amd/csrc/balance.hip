@@ -21,10 +21,12 @@
 // gives each entry's stable rank inside its expert (pos - expert_offset).
 // k_balance_place then runs on G workgroups; each one rebuilds the plan --
 // counts and loads, the per-rank size order of experts (each thread counts the
-// experts that precede its own), the greedy (one thread; the destination
-// cursor only moves forward, so O(E + R + replicas) steps), segment offsets
-// (workgroup scan) -- and remaps its share of entries.  Workgroup 0 writes the
-// per-expert / per-rank / per-segment outputs.
+// experts ahead of its own), every expert's shed amount (parallel: it depends
+// only on its rank's surplus and larger experts), the compacted list of shed
+// pieces (workgroup scan), their merge into destinations (one thread, a
+// forward-only destination cursor held in registers: O(pieces + replicas)
+// steps), segment offsets (workgroup scan) -- and remaps its share of entries.
+// Workgroup 0 writes the per-expert / per-rank / per-segment outputs.
 #include "moe_kernels.h"
 
 namespace moe {
@@ -32,19 +34,24 @@ namespace {
 
 struct BalanceLds {
     int cnt[kMaxE];           // entries per expert
+    int eoff_std[kMaxE];      // plain layout's expert offsets
     int home[kMaxE];          // entries that stay on the owner
     int order[kMaxE];         // experts of each rank, largest first
     int first_rep[kMaxE];     // first replica of each expert (creation order)
     int nrep_e[kMaxE];
-    int room[kMaxE];          // quota - current rows, per rank (R <= E)
-    int slots_used[kMaxE];
+    int room[kMaxE];          // quota - load, per rank (R <= E)
+    int piece_e[kMaxE];       // shed pieces in planning order: expert, amount
+    int piece_n[kMaxE];
+    int dest_r[kMaxE];        // ranks below their quota, ascending, and their room
+    int dest_room[kMaxE];
+    int ndest;
     int rep_e[kMaxBalanceSlots];
     int rep_n[kMaxBalanceSlots];
     int rep_rs[kMaxBalanceSlots];    // (destination rank << 8) | slot
     int slot_rep[kMaxBalanceSlots];  // replica held by (rank, slot), -1 if none
     int seg_off[kMaxE + kMaxBalanceSlots + 1];
     int2 tmp[kLayoutWaves];
-    int nrep;
+    int npiece;
     int flags;
 };
 
@@ -56,26 +63,24 @@ __global__ __launch_bounds__(kLayoutThreads) void k_balance_place(BalanceArgs b)
     // counts from the plain layout, loads and quotas
     for (int e = tid; e < E; e += kLayoutThreads) {
         L.cnt[e] = b.tpe_std[e];
+        L.eoff_std[e] = b.eoff_std[e];
         L.home[e] = L.cnt[e];
         L.first_rep[e] = 0;
         L.nrep_e[e] = 0;
     }
     for (int q = tid; q < R * B; q += kLayoutThreads) L.slot_rep[q] = -1;
-    if (tid == 0) {
-        L.nrep = 0;
-        L.flags = b.status_std[0];
-    }
+    if (tid == 0) L.flags = b.status_std[0];
     __syncthreads();
     const int valid = b.eoff_std[E];
     for (int r = tid; r < R; r += kLayoutThreads) {
         int load = 0;
         for (int j = 0; j < epr; ++j) load += L.cnt[r * epr + j];
         L.room[r] = valid / R + (r < valid % R ? 1 : 0) - load;
-        L.slots_used[r] = 0;
     }
-    // position of each expert in its rank's size order (count desc, id asc)
-    for (int e = tid; e < E; e += kLayoutThreads) {
-        const int r0 = (e / epr) * epr, c = L.cnt[e];
+    __syncthreads();
+    // each expert's place in its rank's size order (count desc, id asc)
+    if (tid < E) {
+        const int e = tid, r0 = (e / epr) * epr, c = L.cnt[e];
         int before = 0;
         for (int j = r0; j < r0 + epr; ++j) {
             const int cj = L.cnt[j];
@@ -84,40 +89,103 @@ __global__ __launch_bounds__(kLayoutThreads) void k_balance_place(BalanceArgs b)
         L.order[r0 + before] = e;
     }
     __syncthreads();
+    // Entries each expert sheds: its rank's surplus minus the counts of the
+    // rank's larger experts, clamped to [0, count] -- what the sequential plan
+    // takes from it as long as destinations do not run out.  The non-zero
+    // pieces are compacted in planning order (ranks ascending, size order).
+    {
+        // counts in planning order, scanned: larger = prefix - prefix at the rank's start
+        const int c = tid < E ? L.cnt[L.order[tid]] : 0;
+        int2 tot0;
+        const int2 pre = block_exclusive_scan2(make_int2(c, 0), L.tmp, tot0);
+        if (tid < E) L.piece_n[tid] = pre.x;     // scratch: prefix of counts in order
+        __syncthreads();
+        int my = 0;
+        if (tid < E) {
+            const int r = L.order[tid] / epr;
+            const int larger = pre.x - L.piece_n[r * epr];
+            my = -L.room[r] - larger;
+            my = my < 0 ? 0 : (my > c ? c : my);
+        }
+        __syncthreads();
+        int2 total;
+        const int2 ex = block_exclusive_scan2(make_int2(my > 0 ? 1 : 0, 0), L.tmp, total);
+        if (tid < E && my > 0) {
+            L.piece_e[ex.x] = L.order[tid];
+            L.piece_n[ex.x] = my;
+        }
+        if (tid == 0) L.npiece = total.x;
+        // destinations: ranks below their quota, ascending
+        const int room = tid < R ? L.room[tid] : 0;
+        int2 dtot;
+        const int2 dex = block_exclusive_scan2(make_int2(room > 0 ? 1 : 0, 0), L.tmp, dtot);
+        if (tid < R && room > 0) {
+            L.dest_r[dex.x] = tid;
+            L.dest_room[dex.x] = room;
+        }
+        if (tid == 0) L.ndest = B > 0 ? dtot.x : 0;
+    }
+    __syncthreads();
 
-    // the greedy plan (one thread)
+    // Merge the pieces into the destinations in order (one thread).  The
+    // cursors only move forward; the next piece and the next destination are
+    // read one step ahead, so the loop carries no LDS read latency, and each
+    // expert's results are written once, when its piece ends.
     if (tid == 0) {
-        int dst = 0, nrep = 0, flags = L.flags;
-        for (int r = 0; r < R && !(flags & FLAG_UNBALANCED); ++r) {
-            int surplus = -L.room[r];
-            for (int j = 0; j < epr && surplus > 0; ++j) {
-                const int e = L.order[r * epr + j];
-                int shed = L.home[e] < surplus ? L.home[e] : surplus;
-                while (shed > 0) {
-                    while (dst < R && (L.room[dst] <= 0 || L.slots_used[dst] >= B)) ++dst;
-                    if (dst == R) {
-                        flags |= FLAG_UNBALANCED;
-                        break;
-                    }
-                    const int take = shed < L.room[dst] ? shed : L.room[dst];
-                    const int slot = L.slots_used[dst]++;
-                    if (L.nrep_e[e] == 0) L.first_rep[e] = nrep;
-                    L.nrep_e[e] += 1;
-                    L.rep_e[nrep] = e;
-                    L.rep_n[nrep] = take;
-                    L.rep_rs[nrep] = (dst << 8) | slot;
-                    L.slot_rep[dst * B + slot] = nrep;
-                    ++nrep;
-                    L.room[dst] -= take;
-                    L.home[e] -= take;
-                    shed -= take;
-                    surplus -= take;
-                    L.room[r] += take;
-                }
-                if (flags & FLAG_UNBALANCED) break;
+        const int npiece = L.npiece, ndest = L.ndest;
+        int flags = L.flags, nrep = 0;
+        int pc = 0, e = 0, left = 0, moved = 0, first = 0;
+        int ne = 0, nleft = 0;
+        if (npiece > 0) {
+            e = L.piece_e[0];
+            left = L.piece_n[0];
+            if (npiece > 1) { ne = L.piece_e[1]; nleft = L.piece_n[1]; }
+        }
+        int di = 0, dr = 0, droom = 0, dslots = 0, ndr = 0, ndroom = 0;
+        if (ndest > 0) {
+            dr = L.dest_r[0];
+            droom = L.dest_room[0];
+            if (ndest > 1) { ndr = L.dest_r[1]; ndroom = L.dest_room[1]; }
+        }
+        while (pc < npiece) {
+            if (di >= ndest) {
+                flags |= FLAG_UNBALANCED;
+                break;
+            }
+            const int take = left < droom ? left : droom;
+            L.rep_e[nrep] = e;
+            L.rep_n[nrep] = take;
+            L.rep_rs[nrep] = (dr << 8) | dslots;
+            L.slot_rep[dr * B + dslots] = nrep;
+            ++nrep;
+            ++dslots;
+            droom -= take;
+            left -= take;
+            moved += take;
+            if (droom == 0 || dslots == B) {        // destination full: next one
+                ++di;
+                dr = ndr;
+                droom = ndroom;
+                dslots = 0;
+                if (di + 1 < ndest) { ndr = L.dest_r[di + 1]; ndroom = L.dest_room[di + 1]; }
+            }
+            if (left == 0) {                         // piece done: record, next piece
+                L.home[e] = L.cnt[e] - moved;
+                L.first_rep[e] = first;
+                L.nrep_e[e] = nrep - first;
+                ++pc;
+                e = ne;
+                left = nleft;
+                moved = 0;
+                first = nrep;
+                if (pc + 1 < npiece) { ne = L.piece_e[pc + 1]; nleft = L.piece_n[pc + 1]; }
             }
         }
-        L.nrep = nrep;
+        if (pc < npiece && moved > 0) {              // stopped inside a piece
+            L.home[e] = L.cnt[e] - moved;
+            L.first_rep[e] = first;
+            L.nrep_e[e] = nrep - first;
+        }
         L.flags = flags;
     }
     __syncthreads();
@@ -171,7 +239,7 @@ __global__ __launch_bounds__(kLayoutThreads) void k_balance_place(BalanceArgs b)
         const int e = b.idx[i];
         int row = -1;
         if (e >= 0 && e < E) {
-            int k = b.pos_std[i] - b.eoff_std[e];
+            int k = b.pos_std[i] - L.eoff_std[e];
             if (k < L.home[e]) {
                 row = L.seg_off[(e / epr) * nseg + (e % epr)] + k;
             } else {

@@ -55,7 +55,7 @@ constexpr int kFusedDispatchMaxN = 4096;
 constexpr int kFusedDispatchThreads = 256;
 
 // balanced layout: at most this many redundant-expert slots in total (R*B)
-constexpr int kMaxBalanceSlots = 1024;
+constexpr int kMaxBalanceSlots = 512;
 constexpr int kMaxSlotsPerRank = 64;
 enum { FLAG_UNBALANCED = 4 };
 

@@ -186,7 +186,7 @@ moe_status moe_combine(const moe_layout_desc *desc, const moe_layout_bufs *layou
  * (t*K+k order) stay home, later ones fill its replicas in creation order.
  * If slots run out the rest stays home and status bit 4 is set.
  *   desc       pad_mode must be MOE_PAD_NONE; rows used <= S*K (src has S*K).
- *   slots_per_rank  B, 0..64, R*B <= 1024.
+ *   slots_per_rank  B, 0..64, R*B <= 512.
  *   out        as moe_layout; expert_offset[e] = first row of e's home segment,
  *              expert_offset[E] = rows used; tokens_per_rank = rows per rank.
  *   bal        seg_offset [R*(E/R+B)+1]: first row of each (rank, segment),
