@@ -120,6 +120,10 @@ EDGE = [
     (_case("multi-zipf", 8192, 64, 256, 8, 8, PAD_MULTIPLE, 128), False, "zipf", False),
     (_case("multi-K16-E1024", 2048, 128, 1024, 16, 1), True, None, False),
     (_case("pad-multiple-1", 50, 8, 4, 2, 2, PAD_MULTIPLE, 1), False, None, False),
+    # largest layout tiles (S*K > 262144 -> 4096-entry tiles), non-power-of-two E
+    (_case("tiles-4096-E96-R3", 37500, 8, 96, 8, 3, PAD_MULTIPLE, 5), False, None, False),
+    # 2048-entry tiles with a capacity that some experts exceed
+    (_case("tiles-2048-capacity", 20000, 16, 40, 5, 5, PAD_CAPACITY, 2500), False, None, False),
 ]
 
 
@@ -460,6 +464,7 @@ BAL = [
     ("one-rank", 500, 2, 16, 1, 4, "pow"),
     ("no-slots", 700, 3, 24, 4, 0, "pow"),
     ("E1024-R8-B64", 2000, 8, 1024, 8, 64, "pow"),
+    ("big-N100000-E96-R6", 12500, 8, 96, 6, 8, "pow"),
     ("empty", 0, 4, 16, 4, 2, "pow"),
 ]
 
