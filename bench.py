@@ -398,7 +398,7 @@ def main(argv=None):
         "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
         "config": {"workload": cfg.name, "S": cfg.S, "H": cfg.H, "E": cfg.E, "K": cfg.K, "R": cfg.R,
                    "fp8_dispatch": cfg.fp8, "routing": cfg.routing, "pad_mode": cfg.pad_mode,
-                   "pad_rows": cfg.pad_rows, "shared": cfg.shared, "parallelism": "ep8 simulated on 1 GPU"},
+                   "pad_rows": cfg.pad_rows, "shared": cfg.shared, "parallelism": f"ep{cfg.R} simulated on 1 GPU"},
         "roofline": roofline, "cpu_baseline": cpu, "kernels": extra, "decode": decode,
         "cu_budget": cu_budget, "balanced_layout": balanced,
     }

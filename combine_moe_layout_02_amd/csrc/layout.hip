@@ -16,10 +16,13 @@
 // A column scan over the 16 per-wave counters then orders the waves.  Nothing
 // depends on the order in which waves or workgroups run.
 //
-// Two variants (thresholds measured on MI355X):
+// Three variants (thresholds measured on MI355X):
 //   single (S*K <= 2048): one 1024-thread workgroup does everything in one
 //          launch.  Above that one CU cannot issue the scattered src stores
 //          fast enough.
+//   onepass (S*K <= 32768): one launch, one workgroup per 1024-entry tile,
+//          each counting all other tiles itself (k_layout_onepass).  Its
+//          counting grows with S*K: beyond 32 tiles two launches are faster.
 //   multi  : k_layout_local ranks tiles of 1024*J entries, one workgroup per
 //          tile, and writes a per-tile histogram; k_layout_place (one
 //          workgroup per tile again) rebuilds the expert offsets from all tile
@@ -28,22 +31,38 @@
 #include "moe_kernels.h"
 
 namespace moe {
+
+constexpr int kOnePassMaxN = 32768;  // one-launch layout up to 32 tiles of 1024 entries
+
 namespace {
 
-// Ranks J*64 consecutive entries from `base` for this wave.  s_wcnt is the
-// wave's [E] counter row (zero on entry; the wave's per-expert totals on exit).
-// key[j] = expert id or -1 (absent / out of range); local[j] = number of this
-// wave's earlier entries with the same expert.
+// This lane's J entries of the wave's J*64 consecutive ones from `base`
+// (expert ids; entries past N read as 0 and are masked later).  Issued before
+// the workgroup clears its counters, so the load latency overlaps that work.
 template <int J>
-__device__ __forceinline__ void wave_rank(const int32_t *__restrict__ idx, int N, int E, int nbits,
-                                          int base, unsigned short *s_wcnt, int (&key)[J],
-                                          int (&local)[J], int &flags) {
+__device__ __forceinline__ void load_keys(const int32_t *__restrict__ idx, int N, int base, int (&raw)[J]) {
+    const int lane = threadIdx.x & (kWave - 1);
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+        const int i = base + j * kWave + lane;
+        raw[j] = i < N ? idx[i] : 0;
+    }
+}
+
+// Ranks the wave's J*64 entries from `base` (raw = load_keys' values).  s_wcnt
+// is the wave's [E] counter row (zero on entry; the wave's per-expert totals
+// on exit).  key[j] = expert id or -1 (absent / out of range); local[j] =
+// number of this wave's earlier entries with the same expert.
+template <int J>
+__device__ __forceinline__ void wave_rank(const int (&raw)[J], int N, int E, int nbits, int base,
+                                          unsigned short *s_wcnt, int (&key)[J], int (&local)[J],
+                                          int &flags) {
     const int lane = threadIdx.x & (kWave - 1);
 #pragma unroll
     for (int j = 0; j < J; ++j) {
         const int i = base + j * kWave + lane;
         const bool in = i < N;
-        const int e = in ? idx[i] : 0;
+        const int e = raw[j];
         const bool ok = in && e >= 0 && e < E;
         if (in && !ok) flags |= FLAG_BAD_EXPERT;
         const uint64_t m = match_key(e, ok, nbits);
@@ -131,13 +150,15 @@ __global__ __launch_bounds__(kLayoutThreads) void k_layout_fused(LayoutArgs a) {
     __shared__ int2 s_tmp[kLayoutWaves];
     __shared__ int s_flags;
     const int tid = threadIdx.x, wave = tid / kWave, lane = tid & (kWave - 1);
+    const int base = wave * kWave * J;
+    int raw[J];
+    load_keys<J>(a.idx, a.N, base, raw);
     for (int x = tid; x < kLayoutWaves * a.E; x += kLayoutThreads) s_cnt[x] = 0;
     if (tid == 0) s_flags = 0;
     __syncthreads();
 
     int key[J], local[J], flags = 0;
-    const int base = wave * kWave * J;
-    wave_rank<J>(a.idx, a.N, a.E, a.nbits, base, s_cnt + wave * a.E, key, local, flags);
+    wave_rank<J>(raw, a.N, a.E, a.nbits, base, s_cnt + wave * a.E, key, local, flags);
     __syncthreads();
     const int cnt = tid < a.E ? column_scan(s_cnt, a.E, tid) : 0;
     flags |= finish_counts(a, cnt, s_off, s_pex, s_tmp, true, 0, 1);  // synchronises the workgroup
@@ -165,13 +186,15 @@ __global__ __launch_bounds__(kLayoutThreads) void k_layout_local(LayoutArgs a) {
     extern __shared__ unsigned short s_cnt[];  // [kLayoutWaves][E]
     __shared__ int s_flags;
     const int tid = threadIdx.x, wave = tid / kWave, lane = tid & (kWave - 1);
+    const int base = blockIdx.x * kLayoutThreads * J + wave * kWave * J;
+    int raw[J];
+    load_keys<J>(a.idx, a.N, base, raw);
     for (int x = tid; x < kLayoutWaves * a.E; x += kLayoutThreads) s_cnt[x] = 0;
     if (tid == 0) s_flags = 0;
     __syncthreads();
 
     int key[J], local[J], flags = 0;
-    const int base = blockIdx.x * kLayoutThreads * J + wave * kWave * J;
-    wave_rank<J>(a.idx, a.N, a.E, a.nbits, base, s_cnt + wave * a.E, key, local, flags);
+    wave_rank<J>(raw, a.N, a.E, a.nbits, base, s_cnt + wave * a.E, key, local, flags);
     if (flags) atomicOr(&s_flags, flags);
     __syncthreads();
     if (tid < a.E) a.blk_hist[static_cast<size_t>(blockIdx.x) * a.E + tid] = column_scan(s_cnt, a.E, tid);
@@ -192,25 +215,33 @@ __global__ __launch_bounds__(kLayoutThreads) void k_layout_place(LayoutArgs a) {
     __shared__ int2 s_tmp[kLayoutWaves];
     __shared__ int s_flags;
     const int tid = threadIdx.x, b = blockIdx.x;
+    // this tile's expert ids and tile ranks, loaded first: nothing below
+    // changes them before they are used
+    int e_in[J], rank_in[J];
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+        const int i = b * kLayoutThreads * J + j * kLayoutThreads + tid;
+        e_in[j] = i < a.N ? a.idx[i] : -1;
+        rank_in[j] = i < a.N ? a.pos[i] : -1;
+    }
     if (tid == 0) s_flags = 0;
     int cnt = 0;
     if (tid < a.E) {
-        // expert tid: entries in tiles before b (in tile order), and in all tiles
-        int pre = 0, t = 0;
-        for (; t + 8 <= a.nblk; t += 8) {
-            int c[8];
+        // expert tid: entries in tiles before b (in tile order), and in all
+        // tiles.  Up to 32 histogram loads in flight at once: the histograms
+        // were written by other XCDs, so each round trip misses this L2.
+        constexpr int kBatch = 32;
+        int pre = 0;
+        for (int t = 0; t < a.nblk; t += kBatch) {
+            int c[kBatch];
 #pragma unroll
-            for (int u = 0; u < 8; ++u) c[u] = a.blk_hist[static_cast<size_t>(t + u) * a.E + tid];
+            for (int u = 0; u < kBatch; ++u)
+                c[u] = t + u < a.nblk ? a.blk_hist[static_cast<size_t>(t + u) * a.E + tid] : 0;
 #pragma unroll
-            for (int u = 0; u < 8; ++u) {
+            for (int u = 0; u < kBatch; ++u) {
                 pre += (t + u < b) ? c[u] : 0;
                 cnt += c[u];
             }
-        }
-        for (; t < a.nblk; ++t) {
-            const int c = a.blk_hist[static_cast<size_t>(t) * a.E + tid];
-            pre += (t < b) ? c : 0;
-            cnt += c;
         }
         s_pre[tid] = pre;
     }
@@ -224,9 +255,9 @@ __global__ __launch_bounds__(kLayoutThreads) void k_layout_place(LayoutArgs a) {
     for (int j = 0; j < J; ++j) {
         const int i = b * kLayoutThreads * J + j * kLayoutThreads + tid;
         if (i >= a.N) break;
-        const int e = a.idx[i];
+        const int e = e_in[j];
         if (e < 0 || e >= a.E) continue;  // already -1
-        const int within = s_pre[e] + a.pos[i];
+        const int within = s_pre[e] + rank_in[j];
         int p = -1;
         if (!(a.pad_mode == PAD_CAPACITY && within >= a.pad_rows)) p = s_off[e] + within;
         a.pos[i] = p;
@@ -239,6 +270,83 @@ __global__ __launch_bounds__(kLayoutThreads) void k_layout_place(LayoutArgs a) {
     }
 }
 
+// One-launch layout for mid-sized batches (tiles of 1024 entries, one
+// workgroup each).  Workgroup b ranks its own tile as k_layout_local does and
+// counts every other tile's entries itself (LDS atomics into "before b" and
+// "after b" counters), so without any exchange between workgroups it knows
+// the per-expert totals and the entries of earlier tiles; then it places its
+// tile as k_layout_place does.  The redundant counting costs one coalesced
+// load per thread per tile, served from L2 once the first workgroups have
+// touched topk_idx.
+__global__ __launch_bounds__(kLayoutThreads) void k_layout_onepass(LayoutArgs a) {
+    extern __shared__ unsigned short s_cnt[];  // [kLayoutWaves][E]
+    __shared__ int s_off[kMaxE + 1], s_pex[kMaxE + 1], s_before[kMaxE], s_after[kMaxE];
+    __shared__ int2 s_tmp[kLayoutWaves];
+    __shared__ int s_flags;
+    const int tid = threadIdx.x, wave = tid / kWave, lane = tid & (kWave - 1), b = blockIdx.x;
+    const int nblk = gridDim.x;
+    const int base = b * kLayoutThreads + wave * kWave;
+    int raw[1];
+    load_keys<1>(a.idx, a.N, base, raw);
+    for (int x = tid; x < kLayoutWaves * a.E; x += kLayoutThreads) s_cnt[x] = 0;
+    for (int e = tid; e < a.E; e += kLayoutThreads) {
+        s_before[e] = 0;
+        s_after[e] = 0;
+    }
+    if (tid == 0) s_flags = 0;
+    __syncthreads();
+
+    int flags = 0;
+    constexpr int kBatch = 16;  // loads in flight per thread
+    for (int t0 = 0; t0 < nblk; t0 += kBatch) {
+        int ev[kBatch];
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+            const int t = t0 + u, i = t * kLayoutThreads + tid;
+            ev[u] = (t < nblk && t != b && i < a.N) ? a.idx[i] : 0;
+        }
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+            const int t = t0 + u, i = t * kLayoutThreads + tid;
+            if (t < nblk && t != b && i < a.N) {
+                const int e = ev[u];
+                if (e >= 0 && e < a.E)
+                    atomicAdd(t < b ? &s_before[e] : &s_after[e], 1);
+                else
+                    flags |= FLAG_BAD_EXPERT;
+            }
+        }
+    }
+    int key[1], local[1];
+    wave_rank<1>(raw, a.N, a.E, a.nbits, base, s_cnt + wave * a.E, key, local, flags);
+    __syncthreads();
+    const int cnt = tid < a.E ? column_scan(s_cnt, a.E, tid) + s_before[tid] + s_after[tid] : 0;
+    flags |= finish_counts(a, cnt, s_off, s_pex, s_tmp, b == 0, b, nblk);  // synchronises the workgroup
+
+    const int i = base + lane;
+    if (i < a.N) {
+        int p = -1;
+        const int e = key[0];
+        if (e >= 0) {
+            const int within = s_before[e] + s_cnt[wave * a.E + e] + local[0];
+            if (!(a.pad_mode == PAD_CAPACITY && within >= a.pad_rows)) p = s_off[e] + within;
+        }
+        a.pos[i] = p;
+        if (p >= 0) a.src[p] = i;
+    }
+    if (b == 0) {  // workgroup 0 has seen every entry: it reports the status
+        if (flags) atomicOr(&s_flags, flags);
+        __syncthreads();
+        if (tid == 0) a.status[0] = s_flags;
+    }
+}
+
+hipError_t launch_onepass(const LayoutArgs &a, size_t lds, hipStream_t s) {
+    const int nblk = (a.N + kLayoutThreads - 1) / kLayoutThreads;
+    hipLaunchKernelGGL(k_layout_onepass, dim3(nblk), dim3(kLayoutThreads), lds, s, a);
+    return hipGetLastError();
+}
+
 template <int J>
 hipError_t launch_fused(const LayoutArgs &a, size_t lds, hipStream_t s) {
     hipLaunchKernelGGL(k_layout_fused<J>, dim3(1), dim3(kLayoutThreads), lds, s, a);
@@ -248,7 +356,7 @@ hipError_t launch_fused(const LayoutArgs &a, size_t lds, hipStream_t s) {
 }  // namespace
 
 size_t layout_workspace_bytes(int64_t N, int E) {
-    if (N <= kSingleMaxN) return 0;
+    if (N <= kOnePassMaxN) return 0;
     const int64_t tile = static_cast<int64_t>(kLayoutThreads) * multi_tile_j(N);
     const int64_t nblk = (N + tile - 1) / tile;
     const size_t bytes = static_cast<size_t>(nblk) * E * sizeof(int32_t) + static_cast<size_t>(nblk) * sizeof(int32_t);
@@ -273,6 +381,7 @@ hipError_t launch_layout(const LayoutArgs &a, hipStream_t s) {
         if (a.N <= kLayoutThreads) return launch_fused<1>(a, lds, s);
         return launch_fused<2>(a, lds, s);
     }
+    if (a.N <= kOnePassMaxN) return launch_onepass(a, lds, s);
     switch (multi_tile_j(a.N)) {
         case 1: return launch_multi<1>(a, lds, s);
         case 2: return launch_multi<2>(a, lds, s);

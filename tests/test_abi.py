@@ -46,7 +46,8 @@ def test_max_recv_rows_and_workspace(moe):
     assert moe.moe_max_recv_rows(moe.LayoutDesc(128, 8, 256, 8, moe.MOE_PAD_CAPACITY, 128)) == 32768
     assert moe.moe_max_recv_rows(moe.LayoutDesc(4096, 8, 256, 8, moe.MOE_PAD_MULTIPLE, 128)) == 65280
     assert moe.moe_layout_workspace_bytes(moe.LayoutDesc(128, 8, 256, 8)) == 0
-    assert moe.moe_layout_workspace_bytes(moe.LayoutDesc(4096, 8, 256, 8)) >= 8 * 256 * 4
+    assert moe.moe_layout_workspace_bytes(moe.LayoutDesc(4096, 8, 256, 8)) == 0      # one launch, no scratch
+    assert moe.moe_layout_workspace_bytes(moe.LayoutDesc(4097, 8, 256, 8)) >= 33 * 256 * 4
     for bad in [moe.LayoutDesc(8, 2, 8, 3), moe.LayoutDesc(8, 0, 8, 1), moe.LayoutDesc(8, 17, 32, 1),
                 moe.LayoutDesc(8, 2, 1025, 1), moe.LayoutDesc(8, 2, 8, 2, moe.MOE_PAD_MULTIPLE, 0),
                 moe.LayoutDesc(-1, 2, 8, 2), moe.LayoutDesc(8, 2, 8, 2, 7, 1),
@@ -80,7 +81,7 @@ def test_layout_argument_errors(moe):
     assert lib.moe_layout(ctypes.byref(d), P(FAKE), ctypes.byref(nb), None, 0, None) == moe.MOE_ERR_NULL
     mb = _bufs(moe, misalign="pos")
     assert lib.moe_layout(ctypes.byref(d), P(FAKE), ctypes.byref(mb), None, 0, None) == moe.MOE_ERR_ALIGN
-    big = moe.LayoutDesc(4096, 8, 256, 8).c()
+    big = moe.LayoutDesc(8192, 8, 256, 8).c()
     need = lib.moe_layout_workspace_bytes(ctypes.byref(big))
     assert need > 0
     assert lib.moe_layout(ctypes.byref(big), P(FAKE), ctypes.byref(b), None, 0, None) == moe.MOE_ERR_WORKSPACE
