@@ -11,8 +11,9 @@ constexpr int kWave = 64;
 constexpr int kLayoutThreads = 1024;              // 16 waves per layout workgroup
 constexpr int kLayoutWaves = kLayoutThreads / kWave;
 // Layout variant by batch size (entries N = S*K), from measurements on MI355X:
-// one workgroup up to 2048 entries; above, two launches over tiles of
-// 1024*J entries, J = 1 up to 65536 entries, 2 up to 262144, 4 beyond.
+// one workgroup up to 2048 entries; one launch over 1024-entry tiles up to
+// 32768; above, two launches over tiles of 1024*J entries, J = 1 up to 65536
+// entries, 2 up to 262144, 4 beyond.
 constexpr int kSingleMaxN = 2048;
 inline int multi_tile_j(int64_t N) { return N <= 65536 ? 1 : (N <= 262144 ? 2 : 4); }
 constexpr int kMaxE = 1024;
