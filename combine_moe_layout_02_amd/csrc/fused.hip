@@ -27,6 +27,7 @@ namespace {
 
 constexpr int kT = kFusedDispatchThreads;
 constexpr int kTW = kT / kWave;
+constexpr int kPerThread = kFusedDispatchMaxN / kT;  // routing entries per thread, at most
 
 struct SmallLayoutLds {
     int cnt[kMaxE];       // entries per expert, all tokens
@@ -37,9 +38,20 @@ struct SmallLayoutLds {
     int flags;
 };
 
+// This thread's routing entries (tid, tid + kT, ...), all loads in flight
+// at once; entries past N read as 0 and are skipped by small_layout.
+__device__ __forceinline__ void load_routing(const LayoutArgs &a, int (&ev)[kPerThread]) {
+#pragma unroll
+    for (int u = 0; u < kPerThread; ++u) {
+        const int i = threadIdx.x + u * kT;
+        ev[u] = i < a.N ? a.idx[i] : 0;
+    }
+}
+
 // Counts, padded offsets, count-only outputs (workgroup 0) and this
-// workgroup's share of padding rows.  Returns this thread's flags.
-__device__ int small_layout(const LayoutArgs &a, int t, int K, SmallLayoutLds &L) {
+// workgroup's share of padding rows, from load_routing's values.  Returns this
+// thread's flags.
+__device__ int small_layout(const LayoutArgs &a, int t, int K, const int (&ev)[kPerThread], SmallLayoutLds &L) {
     const int tid = threadIdx.x;
     for (int e = tid; e < a.E; e += kT) {
         L.cnt[e] = 0;
@@ -48,8 +60,11 @@ __device__ int small_layout(const LayoutArgs &a, int t, int K, SmallLayoutLds &L
     __syncthreads();
     int flags = 0;
     const int before = t * K;
-    for (int i = tid; i < a.N; i += kT) {
-        const int e = a.idx[i];
+#pragma unroll
+    for (int u = 0; u < kPerThread; ++u) {
+        const int i = tid + u * kT;
+        if (i >= a.N) break;
+        const int e = ev[u];
         if (e < 0 || e >= a.E) {
             flags |= FLAG_BAD_EXPERT;
             continue;
@@ -122,12 +137,18 @@ __device__ int small_layout(const LayoutArgs &a, int t, int K, SmallLayoutLds &L
     return flags;
 }
 
-// Rows of token t's K entries (-1 if not placed).  Wave-uniform.
+// Token t's K expert ids (wave-uniform loads, issued at kernel entry).
 template <int K>
-__device__ __forceinline__ void token_rows(const LayoutArgs &a, int t, const SmallLayoutLds &L, int (&p)[K]) {
-    int e[K];
+__device__ __forceinline__ void token_experts(const LayoutArgs &a, int t, int (&e)[K]) {
 #pragma unroll
     for (int k = 0; k < K; ++k) e[k] = a.idx[static_cast<size_t>(t) * K + k];
+}
+
+// Rows of token t's K entries (-1 if not placed) from its expert ids e.
+// Wave-uniform.
+template <int K>
+__device__ __forceinline__ void token_rows(const LayoutArgs &a, const int (&e)[K], const SmallLayoutLds &L,
+                                           int (&p)[K]) {
 #pragma unroll
     for (int k = 0; k < K; ++k) {
         int row = -1;
@@ -171,10 +192,13 @@ __global__ __launch_bounds__(kT) void k_layout_dispatch_fp8(LayoutArgs la, Dispa
         lo = hid[2 * g];
         hi = hid[2 * g + 1];
     }
+    int ev[kPerThread], e[K];
+    load_routing(la, ev);
+    token_experts<K>(la, t, e);
     if (threadIdx.x == 0) L.flags = 0;
-    const int flags = small_layout(la, t, K, L);
+    const int flags = small_layout(la, t, K, ev, L);
     int p[K];
-    token_rows<K>(la, t, L, p);
+    token_rows<K>(la, e, L, p);
     if (c == 0) write_token_maps<K>(la, da, t, p);
 
     float scale;
@@ -205,10 +229,13 @@ __global__ __launch_bounds__(kT) void k_layout_dispatch_bf16(LayoutArgs la, Disp
     const u32x4 *__restrict__ hid = static_cast<const u32x4 *>(da.hidden) + static_cast<size_t>(t) * nvec;
     u32x4 x = {0u, 0u, 0u, 0u};
     if (active) x = hid[v];
+    int ev[kPerThread], e[K];
+    load_routing(la, ev);
+    token_experts<K>(la, t, e);
     if (threadIdx.x == 0) L.flags = 0;
-    const int flags = small_layout(la, t, K, L);
+    const int flags = small_layout(la, t, K, ev, L);
     int p[K];
-    token_rows<K>(la, t, L, p);
+    token_rows<K>(la, e, L, p);
     if (c == 0) write_token_maps<K>(la, da, t, p);
 
     u32x4 *__restrict__ recv = static_cast<u32x4 *>(da.recv);
