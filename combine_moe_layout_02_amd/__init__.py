@@ -265,7 +265,7 @@ class Balance:
     """Device outputs of moe_layout_balanced beyond the layout."""
     seg_offset: torch.Tensor    # [R*(E/R+B)+1] int32
     slot_expert: torch.Tensor   # [R*B] int32
-    workspace: torch.Tensor     # scratch (uint8)
+    workspace: Optional[torch.Tensor]   # scratch (uint8), None when none is needed
 
     def c(self) -> moe_balance_bufs:
         return moe_balance_bufs(self.seg_offset.data_ptr(), self.slot_expert.data_ptr())
@@ -276,7 +276,7 @@ def alloc_balance(desc: LayoutDesc, slots_per_rank: int, device) -> Balance:
     ws = moe_layout_balanced_workspace_bytes(desc, slots_per_rank)
     return Balance(torch.empty(desc.R * (epr + slots_per_rank) + 1, dtype=torch.int32, device=device),
                    torch.empty(max(desc.R * slots_per_rank, 1), dtype=torch.int32, device=device),
-                   torch.empty(max(ws, 256), dtype=torch.uint8, device=device))
+                   torch.empty(ws, dtype=torch.uint8, device=device) if ws else None)
 
 
 def moe_layout_balanced(desc: LayoutDesc, slots_per_rank: int, topk_idx: torch.Tensor,
@@ -291,7 +291,8 @@ def moe_layout_balanced(desc: LayoutDesc, slots_per_rank: int, topk_idx: torch.T
         balance = alloc_balance(desc, slots_per_rank, dev)
     d, b, bb = desc.c(), layout.c(), balance.c()
     rc = _lib.moe_layout_balanced(ctypes.byref(d), int(slots_per_rank), _ptr(topk_idx), ctypes.byref(b),
-                                  ctypes.byref(bb), _ptr(balance.workspace), balance.workspace.numel(),
+                                  ctypes.byref(bb), _ptr(balance.workspace),
+                                  0 if balance.workspace is None else balance.workspace.numel(),
                                   _stream(stream, dev))
     if rc != MOE_OK:
         raise MoeError(rc, "moe_layout_balanced")

@@ -215,8 +215,8 @@ moe_status moe_layout_balanced(const moe_layout_desc *desc, int32_t slots_per_ra
     if (bal->seg_offset == nullptr || (slots_per_rank > 0 && bal->slot_expert == nullptr)) return MOE_ERR_NULL;
     if (!aligned(bal->seg_offset, 4) || !aligned(bal->slot_expert, 4)) return MOE_ERR_ALIGN;
     const size_t need = moe::balance_workspace_bytes(la.N, desc->E, desc->R);
-    if (workspace == nullptr || workspace_bytes < need) return MOE_ERR_WORKSPACE;
-    if (!aligned(workspace, 256)) return MOE_ERR_ALIGN;
+    if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return MOE_ERR_WORKSPACE;
+    if (need > 0 && !aligned(workspace, 256)) return MOE_ERR_ALIGN;
     moe::BalanceArgs b{};
     b.idx = topk_idx;
     b.N = la.N;

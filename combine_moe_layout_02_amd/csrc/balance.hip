@@ -32,6 +32,24 @@
 namespace moe {
 namespace {
 
+// Entries of the strictly increasing a[0..n) below v / not above v.
+__device__ __forceinline__ int count_below(const int *a, int n, int v) {
+    int lo = 0, hi = n;
+    while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (a[mid] < v) lo = mid + 1; else hi = mid;
+    }
+    return lo;
+}
+__device__ __forceinline__ int count_upto(const int *a, int n, int v) {
+    int lo = 0, hi = n;
+    while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (a[mid] <= v) lo = mid + 1; else hi = mid;
+    }
+    return lo;
+}
+
 struct BalanceLds {
     int cnt[kMaxE];           // entries per expert
     int eoff_std[kMaxE];      // plain layout's expert offsets
@@ -49,40 +67,51 @@ struct BalanceLds {
     int rep_n[kMaxBalanceSlots];
     int rep_rs[kMaxBalanceSlots];    // (destination rank << 8) | slot
     int slot_rep[kMaxBalanceSlots];  // replica held by (rank, slot), -1 if none
+    int mrep[kMaxBalanceSlots];      // parallel merge: replicas before each merged breakpoint
     int seg_off[kMaxE + kMaxBalanceSlots + 1];
     int2 tmp[kLayoutWaves];
     int npiece;
     int flags;
 };
 
-__global__ __launch_bounds__(kLayoutThreads) void k_balance_place(BalanceArgs b) {
-    __shared__ BalanceLds L;
+// The plan, from L.cnt (entries per expert, visible to every thread) and
+// L.flags; valid = entries with an expert in range.  Called by all threads of
+// the workgroup (it synchronises).  Leaves home, first_rep, nrep_e, the
+// replica lists, slot_rep and the segment offsets seg_off in L.
+__device__ __forceinline__ void plan_balance(BalanceLds &L, int E, int R, int B, int valid) {
     const int tid = threadIdx.x;
-    const int E = b.E, R = b.R, B = b.B, epr = E / R, nseg = epr + B, ngrp = R * nseg;
-
-    // counts from the plain layout, loads and quotas
+    const int epr = E / R, nseg = epr + B, ngrp = R * nseg;
     for (int e = tid; e < E; e += kLayoutThreads) {
-        L.cnt[e] = b.tpe_std[e];
-        L.eoff_std[e] = b.eoff_std[e];
         L.home[e] = L.cnt[e];
         L.first_rep[e] = 0;
         L.nrep_e[e] = 0;
     }
     for (int q = tid; q < R * B; q += kLayoutThreads) L.slot_rep[q] = -1;
-    if (tid == 0) L.flags = b.status_std[0];
-    __syncthreads();
-    const int valid = b.eoff_std[E];
     for (int r = tid; r < R; r += kLayoutThreads) {
-        int load = 0;
-        for (int j = 0; j < epr; ++j) load += L.cnt[r * epr + j];
+        int load = 0, j = 0;
+        for (; j + 8 <= epr; j += 8) {   // 8 LDS reads in flight
+            int c8[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) c8[u] = L.cnt[r * epr + j + u];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) load += c8[u];
+        }
+        for (; j < epr; ++j) load += L.cnt[r * epr + j];
         L.room[r] = valid / R + (r < valid % R ? 1 : 0) - load;
     }
     __syncthreads();
     // each expert's place in its rank's size order (count desc, id asc)
     if (tid < E) {
         const int e = tid, r0 = (e / epr) * epr, c = L.cnt[e];
-        int before = 0;
-        for (int j = r0; j < r0 + epr; ++j) {
+        int before = 0, j = r0;
+        for (; j + 8 <= r0 + epr; j += 8) {   // 8 LDS reads in flight
+            int c8[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) c8[u] = L.cnt[j + u];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) before += (c8[u] > c || (c8[u] == c && j + u < e)) ? 1 : 0;
+        }
+        for (; j < r0 + epr; ++j) {
             const int cj = L.cnt[j];
             before += (cj > c || (cj == c && j < e)) ? 1 : 0;
         }
@@ -127,12 +156,68 @@ __global__ __launch_bounds__(kLayoutThreads) void k_balance_place(BalanceArgs b)
     }
     __syncthreads();
 
-    // Merge the pieces into the destinations in order (one thread).  The
-    // cursors only move forward; the next piece and the next destination are
-    // read one step ahead, so the loop carries no LDS read latency, and each
-    // expert's results are written once, when its piece ends.
-    if (tid == 0) {
-        const int npiece = L.npiece, ndest = L.ndest;
+    // Parallel merge of pieces into destinations.  Laid end to end, the
+    // pieces (planning order) and the destinations' rooms (ascending rank)
+    // both cover [0, T): the overloaded ranks' surpluses add up to the other
+    // ranks' rooms.  A replica is a non-empty overlap of one piece's span with
+    // one destination's span, numbered in stream order -- what the sequential
+    // greedy below produces whenever no destination needs more than B slots.
+    // If one would, or the totals differ, the sequential loop runs instead.
+    bool merged = false;
+    const int npiece = L.npiece, ndest = L.ndest;
+    if (npiece > 0 && ndest > 0 && npiece + ndest <= kMaxBalanceSlots) {  // uniform
+        int2 tot;
+        const int2 ex = block_exclusive_scan2(make_int2(tid < npiece ? L.piece_n[tid] : 0,
+                                                        tid < ndest ? L.dest_room[tid] : 0), L.tmp, tot);
+        int *A = L.order, *C = L.room;  // piece and destination starts (both no longer read)
+        if (tid < npiece) A[tid] = ex.x;
+        if (tid < ndest) C[tid] = ex.y;
+        __syncthreads();
+        // merged breakpoints, ties: piece start first (its interval is then empty)
+        const int M = npiece + ndest, T = tot.x;
+        int *mval = L.seg_off;  // scratch until the segment scan
+        if (tid < npiece) mval[tid + count_below(C, ndest, A[tid])] = A[tid];
+        if (tid < ndest) mval[tid + count_upto(A, npiece, C[tid])] = C[tid];
+        __syncthreads();
+        const int len = tid < M ? (tid + 1 < M ? mval[tid + 1] : T) - mval[tid] : 0;
+        int2 rtot;
+        const int2 rex = block_exclusive_scan2(make_int2(len > 0 ? 1 : 0, 0), L.tmp, rtot);
+        if (tid < M) L.mrep[tid] = rex.x;
+        __syncthreads();
+        int q = 0, d = 0, slot = 0;
+        if (len > 0) {
+            q = rex.x;
+            d = count_upto(C, ndest, mval[tid]) - 1;                    // destination holding it
+            slot = q - L.mrep[d + count_upto(A, npiece, C[d])];          // its first replica is slot 0
+        }
+        const bool over = __syncthreads_or((len > 0 && slot >= B) || tot.x != tot.y);
+        if (!over) {
+            if (len > 0) {
+                const int pc = count_upto(A, npiece, mval[tid]) - 1;   // piece holding it
+                const int dr = L.dest_r[d];
+                L.rep_e[q] = L.piece_e[pc];
+                L.rep_n[q] = len;
+                L.rep_rs[q] = (dr << 8) | slot;
+                L.slot_rep[dr * B + slot] = q;
+            }
+            if (tid < npiece) {
+                const int e = L.piece_e[tid];
+                const int first = L.mrep[tid + count_below(C, ndest, A[tid])];
+                const int next = tid + 1 < npiece ? L.mrep[tid + 1 + count_below(C, ndest, A[tid + 1])] : rtot.x;
+                L.home[e] = L.cnt[e] - L.piece_n[tid];
+                L.first_rep[e] = first;
+                L.nrep_e[e] = next - first;
+            }
+            merged = true;
+        }
+        __syncthreads();
+    }
+
+    // Sequential merge (one thread), used when the parallel form does not
+    // apply.  The cursors only move forward; the next piece and the next
+    // destination are read one step ahead, so the loop carries no LDS read
+    // latency, and each expert's results are written once, when its piece ends.
+    if (!merged && tid == 0) {
         int flags = L.flags, nrep = 0;
         int pc = 0, e = 0, left = 0, moved = 0, first = 0;
         int ne = 0, nleft = 0;
@@ -211,50 +296,78 @@ __global__ __launch_bounds__(kLayoutThreads) void k_balance_place(BalanceArgs b)
     if (tid == 0) L.seg_off[ngrp] = total.x;
     __syncthreads();
 
-    // count-only outputs (workgroup 0)
-    if (blockIdx.x == 0) {
-        for (int g = tid; g <= ngrp; g += kLayoutThreads) b.seg_offset[g] = L.seg_off[g];
-        for (int e = tid; e < E; e += kLayoutThreads) {
-            b.tpe[e] = L.cnt[e];
-            b.eoff[e] = L.seg_off[(e / epr) * nseg + (e % epr)];
+}
+
+// Row of the k-th entry (stable t*K+k order) of expert e under the plan:
+// the first home[e] stay in the home segment, the rest fill the replicas in
+// creation order.
+__device__ __forceinline__ int balanced_row(const BalanceLds &L, int e, int k, int epr, int nseg) {
+    if (k < L.home[e]) return L.seg_off[(e / epr) * nseg + (e % epr)] + k;
+    k -= L.home[e];
+    const int q0 = L.first_rep[e], q1 = q0 + L.nrep_e[e];
+    for (int q = q0; q < q1; ++q) {
+        if (k < L.rep_n[q]) {
+            const int rs = L.rep_rs[q];
+            return L.seg_off[(rs >> 8) * nseg + epr + (rs & 0xFF)] + k;
         }
-        for (int r = tid; r < R; r += kLayoutThreads) {
-            b.roff[r] = L.seg_off[r * nseg];
-            b.tpr[r] = L.seg_off[(r + 1) * nseg] - L.seg_off[r * nseg];
-        }
-        for (int q = tid; q < R * B; q += kLayoutThreads) {
-            const int rep = L.slot_rep[q];
-            b.slot_expert[q] = rep >= 0 ? L.rep_e[rep] : -1;
-        }
-        if (tid == 0) {
-            b.eoff[E] = L.seg_off[ngrp];
-            b.roff[R] = L.seg_off[ngrp];
-            b.status[0] = L.flags;
-        }
+        k -= L.rep_n[q];
     }
+    return -1;
+}
+
+// Outputs that depend only on the plan (one workgroup writes them).
+__device__ __forceinline__ void write_balance_counts(const BalanceLds &L, const BalanceArgs &b) {
+    const int tid = threadIdx.x;
+    const int E = b.E, R = b.R, B = b.B, epr = E / R, nseg = epr + B, ngrp = R * nseg;
+    for (int g = tid; g <= ngrp; g += kLayoutThreads) b.seg_offset[g] = L.seg_off[g];
+    for (int e = tid; e < E; e += kLayoutThreads) {
+        b.tpe[e] = L.cnt[e];
+        b.eoff[e] = L.seg_off[(e / epr) * nseg + (e % epr)];
+    }
+    for (int r = tid; r < R; r += kLayoutThreads) {
+        b.roff[r] = L.seg_off[r * nseg];
+        b.tpr[r] = L.seg_off[(r + 1) * nseg] - L.seg_off[r * nseg];
+    }
+    for (int q = tid; q < R * B; q += kLayoutThreads) {
+        const int rep = L.slot_rep[q];
+        b.slot_expert[q] = rep >= 0 ? L.rep_e[rep] : -1;
+    }
+    if (tid == 0) {
+        b.eoff[E] = L.seg_off[ngrp];
+        b.roff[R] = L.seg_off[ngrp];
+        b.status[0] = L.flags;
+    }
+}
+
+// Two-step form: the plain layout ran first (into workspace) and gives each
+// entry's stable rank inside its expert (pos - expert_offset).  G workgroups
+// each rebuild the plan and remap their share of entries.
+__global__ __launch_bounds__(kLayoutThreads) void k_balance_place(BalanceArgs b) {
+    __shared__ BalanceLds L;
+    const int tid = threadIdx.x;
+    const int E = b.E, R = b.R, B = b.B, epr = E / R, nseg = epr + B, ngrp = R * nseg;
+    // Everything read from global memory is requested up front, so the plan
+    // overlaps one round trip: this workgroup's first entries (expert, plain
+    // row) and the valid-entry total.
+    const int stride = gridDim.x * kLayoutThreads;
+    const int i0 = blockIdx.x * kLayoutThreads + tid;
+    const int e_first = i0 < b.N ? b.idx[i0] : -1;
+    const int p_first = i0 < b.N ? b.pos_std[i0] : 0;
+    const int valid = b.eoff_std[E];
+    for (int e = tid; e < E; e += kLayoutThreads) {
+        L.cnt[e] = b.tpe_std[e];
+        L.eoff_std[e] = b.eoff_std[e];
+    }
+    if (tid == 0) L.flags = b.status_std[0];
+    __syncthreads();
+    plan_balance(L, E, R, B, valid);
+    if (blockIdx.x == 0) write_balance_counts(L, b);
 
     // this workgroup's entries: stable rank inside the expert -> balanced row
-    const int stride = gridDim.x * kLayoutThreads;
-    for (int i = blockIdx.x * kLayoutThreads + tid; i < b.N; i += stride) {
-        const int e = b.idx[i];
+    for (int i = i0; i < b.N; i += stride) {
+        const int e = i == i0 ? e_first : b.idx[i];
         int row = -1;
-        if (e >= 0 && e < E) {
-            int k = b.pos_std[i] - L.eoff_std[e];
-            if (k < L.home[e]) {
-                row = L.seg_off[(e / epr) * nseg + (e % epr)] + k;
-            } else {
-                k -= L.home[e];
-                const int q0 = L.first_rep[e], q1 = q0 + L.nrep_e[e];
-                for (int q = q0; q < q1; ++q) {
-                    if (k < L.rep_n[q]) {
-                        const int rs = L.rep_rs[q];
-                        row = L.seg_off[(rs >> 8) * nseg + epr + (rs & 0xFF)] + k;
-                        break;
-                    }
-                    k -= L.rep_n[q];
-                }
-            }
-        }
+        if (e >= 0 && e < E) row = balanced_row(L, e, (i == i0 ? p_first : b.pos_std[i]) - L.eoff_std[e], epr, nseg);
         b.pos[i] = row;
         if (row >= 0) b.src[row] = i;
     }
@@ -262,9 +375,61 @@ __global__ __launch_bounds__(kLayoutThreads) void k_balance_place(BalanceArgs b)
     for (int r = L.seg_off[ngrp] + blockIdx.x * kLayoutThreads + tid; r < b.N; r += stride) b.src[r] = -1;
 }
 
+// One-launch form for batches of up to 32 tiles of 1024 entries, one
+// workgroup per tile.  Each workgroup counts the other tiles itself and ranks
+// its own tile (as the one-launch plain layout does), so it holds every
+// expert's count and each of its entries' stable rank inside its expert with
+// no exchange between workgroups; then it builds the plan and places its own
+// entries.  No plain layout is written or read back.
+__global__ __launch_bounds__(kLayoutThreads) void k_layout_balanced_onepass(LayoutArgs a, BalanceArgs b) {
+    extern __shared__ unsigned short s_cnt[];  // [kLayoutWaves][E]
+    __shared__ int s_before[kMaxE], s_after[kMaxE];
+    __shared__ BalanceLds L;
+    __shared__ int s_bad;
+    const int tid = threadIdx.x, wave = tid / kWave, lane = tid & (kWave - 1), tb = blockIdx.x;
+    const int E = a.E, epr = E / b.R, nseg = epr + b.B, ngrp = b.R * nseg, nblk = gridDim.x;
+    const int base = tb * kLayoutThreads + wave * kWave;
+    int raw[1];
+    load_keys<1>(a.idx, a.N, base, raw);
+    for (int x = tid; x < kLayoutWaves * E; x += kLayoutThreads) s_cnt[x] = 0;
+    for (int e = tid; e < E; e += kLayoutThreads) {
+        s_before[e] = 0;
+        s_after[e] = 0;
+    }
+    if (tid == 0) {
+        s_bad = 0;
+        L.flags = 0;
+    }
+    __syncthreads();
+
+    int flags = 0, bad = 0;
+    count_other_tiles(a.idx, a.N, E, nblk, tb, s_before, s_after, flags, bad);
+    int key[1], local[1];
+    wave_rank<1>(raw, a.N, E, a.nbits, base, s_cnt + wave * E, key, local, flags);
+    if (base + lane < a.N && key[0] < 0) ++bad;
+    if (flags) atomicOr(&L.flags, flags);
+    if (bad) atomicAdd(&s_bad, bad);
+    __syncthreads();
+    if (tid < E) L.cnt[tid] = s_before[tid] + column_scan(s_cnt, E, tid) + s_after[tid];
+    __syncthreads();
+    plan_balance(L, E, b.R, b.B, a.N - s_bad);
+    if (tb == 0) write_balance_counts(L, b);
+
+    const int i = base + lane;
+    if (i < a.N) {
+        const int e = key[0];
+        const int row = e >= 0 ? balanced_row(L, e, s_before[e] + s_cnt[wave * E + e] + local[0], epr, nseg) : -1;
+        b.pos[i] = row;
+        if (row >= 0) b.src[row] = i;
+    }
+    // rows past the valid ones (only when some ids were out of range)
+    for (int r = L.seg_off[ngrp] + tb * kLayoutThreads + tid; r < a.N; r += nblk * kLayoutThreads) b.src[r] = -1;
+}
+
 }  // namespace
 
 size_t balance_workspace_bytes(int64_t N, int E, int R) {
+    if (N <= kOnePassMaxN) return 0;  // one launch, no plain layout to hold
     auto up = [](size_t x) { return (x + 255) / 256 * 256; };
     return up(static_cast<size_t>(N) * 4) * 2 + up(static_cast<size_t>(E) * 4) + up(static_cast<size_t>(R) * 4) +
            up(static_cast<size_t>(E + 1) * 4) + up(static_cast<size_t>(R + 1) * 4) + up(4) +
@@ -272,6 +437,12 @@ size_t balance_workspace_bytes(int64_t N, int E, int R) {
 }
 
 hipError_t launch_layout_balanced(const LayoutArgs &la_in, BalanceArgs b, void *workspace, hipStream_t s) {
+    if (la_in.N <= kOnePassMaxN) {
+        const int nblk = la_in.N > 0 ? (la_in.N + kLayoutThreads - 1) / kLayoutThreads : 1;
+        const size_t lds = static_cast<size_t>(kLayoutWaves) * la_in.E * sizeof(unsigned short);
+        hipLaunchKernelGGL(k_layout_balanced_onepass, dim3(nblk), dim3(kLayoutThreads), lds, s, la_in, b);
+        return hipGetLastError();
+    }
     auto up = [](size_t x) { return (x + 255) / 256 * 256; };
     char *ws = static_cast<char *>(workspace);
     const int64_t N = la_in.N;

@@ -31,62 +31,7 @@
 #include "moe_kernels.h"
 
 namespace moe {
-
-constexpr int kOnePassMaxN = 32768;  // one-launch layout up to 32 tiles of 1024 entries
-
 namespace {
-
-// This lane's J entries of the wave's J*64 consecutive ones from `base`
-// (expert ids; entries past N read as 0 and are masked later).  Issued before
-// the workgroup clears its counters, so the load latency overlaps that work.
-template <int J>
-__device__ __forceinline__ void load_keys(const int32_t *__restrict__ idx, int N, int base, int (&raw)[J]) {
-    const int lane = threadIdx.x & (kWave - 1);
-#pragma unroll
-    for (int j = 0; j < J; ++j) {
-        const int i = base + j * kWave + lane;
-        raw[j] = i < N ? idx[i] : 0;
-    }
-}
-
-// Ranks the wave's J*64 entries from `base` (raw = load_keys' values).  s_wcnt
-// is the wave's [E] counter row (zero on entry; the wave's per-expert totals
-// on exit).  key[j] = expert id or -1 (absent / out of range); local[j] =
-// number of this wave's earlier entries with the same expert.
-template <int J>
-__device__ __forceinline__ void wave_rank(const int (&raw)[J], int N, int E, int nbits, int base,
-                                          unsigned short *s_wcnt, int (&key)[J], int (&local)[J],
-                                          int &flags) {
-    const int lane = threadIdx.x & (kWave - 1);
-#pragma unroll
-    for (int j = 0; j < J; ++j) {
-        const int i = base + j * kWave + lane;
-        const bool in = i < N;
-        const int e = raw[j];
-        const bool ok = in && e >= 0 && e < E;
-        if (in && !ok) flags |= FLAG_BAD_EXPERT;
-        const uint64_t m = match_key(e, ok, nbits);
-        const int r = lanes_below(m);
-        const int before = ok ? static_cast<int>(s_wcnt[e]) : 0;
-        // every lane of the group has read the counter; the lowest one advances it
-        if (ok && r == 0) s_wcnt[e] = static_cast<unsigned short>(before + __popcll(m));
-        key[j] = ok ? e : -1;
-        local[j] = before + r;
-    }
-}
-
-// Per-wave counters of expert e -> exclusive prefixes over waves; returns the
-// workgroup's total for e.
-__device__ __forceinline__ int column_scan(unsigned short *s_cnt, int E, int e) {
-    int run = 0;
-#pragma unroll
-    for (int w = 0; w < kLayoutWaves; ++w) {
-        const int c = s_cnt[w * E + e];
-        s_cnt[w * E + e] = static_cast<unsigned short>(run);
-        run += c;
-    }
-    return run;
-}
 
 // From per-expert counts (thread e < E holds count e): placed rows, padded
 // segment lengths and their exclusive scans (into s_off / s_pex).  With
@@ -296,27 +241,8 @@ __global__ __launch_bounds__(kLayoutThreads) void k_layout_onepass(LayoutArgs a)
     if (tid == 0) s_flags = 0;
     __syncthreads();
 
-    int flags = 0;
-    constexpr int kBatch = 16;  // loads in flight per thread
-    for (int t0 = 0; t0 < nblk; t0 += kBatch) {
-        int ev[kBatch];
-#pragma unroll
-        for (int u = 0; u < kBatch; ++u) {
-            const int t = t0 + u, i = t * kLayoutThreads + tid;
-            ev[u] = (t < nblk && t != b && i < a.N) ? a.idx[i] : 0;
-        }
-#pragma unroll
-        for (int u = 0; u < kBatch; ++u) {
-            const int t = t0 + u, i = t * kLayoutThreads + tid;
-            if (t < nblk && t != b && i < a.N) {
-                const int e = ev[u];
-                if (e >= 0 && e < a.E)
-                    atomicAdd(t < b ? &s_before[e] : &s_after[e], 1);
-                else
-                    flags |= FLAG_BAD_EXPERT;
-            }
-        }
-    }
+    int flags = 0, bad = 0;
+    count_other_tiles(a.idx, a.N, a.E, nblk, b, s_before, s_after, flags, bad);
     int key[1], local[1];
     wave_rank<1>(raw, a.N, a.E, a.nbits, base, s_cnt + wave * a.E, key, local, flags);
     __syncthreads();

@@ -15,6 +15,7 @@ constexpr int kLayoutWaves = kLayoutThreads / kWave;
 // 32768; above, two launches over tiles of 1024*J entries, J = 1 up to 65536
 // entries, 2 up to 262144, 4 beyond.
 constexpr int kSingleMaxN = 2048;
+constexpr int kOnePassMaxN = 32768;  // one launch up to 32 tiles of 1024 entries
 inline int multi_tile_j(int64_t N) { return N <= 65536 ? 1 : (N <= 262144 ? 2 : 4); }
 constexpr int kMaxE = 1024;
 constexpr int kMaxK = 16;
@@ -145,16 +146,25 @@ __device__ __forceinline__ uint64_t match_key(int key, bool active, int nbits) {
     return m;
 }
 
+// Inclusive prefix sum of an int across the 64 lanes of a wave, with DPP
+// (data-parallel primitives on VALU operands, no LDS round trip): shifts by
+// 1, 2, 4 and 8 lanes inside each row of 16 (lanes shifted in from outside the
+// row add 0), then lane 15's sum is added to row 1 and lane 47's to row 3,
+// then lane 31's to rows 2 and 3.  On MI355X about 100 cycles against ~480 for
+// the same scan through six cross-lane shuffles.
+__device__ __forceinline__ int wave_inclusive_scan(int v) {
+    v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, false);  // row_shr:1
+    v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, false);  // row_shr:2
+    v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, false);  // row_shr:4
+    v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, false);  // row_shr:8
+    v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);  // row_bcast:15 -> rows 1, 3
+    v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);  // row_bcast:31 -> rows 2, 3
+    return v;
+}
+
 // Inclusive prefix sum of an int pair across the 64 lanes of a wave.
 __device__ __forceinline__ int2 wave_inclusive_scan2(int2 v) {
-    const int lane = threadIdx.x & (kWave - 1);
-#pragma unroll
-    for (int d = 1; d < kWave; d <<= 1) {
-        const int ax = __shfl_up(v.x, d, kWave);
-        const int ay = __shfl_up(v.y, d, kWave);
-        if (lane >= d) { v.x += ax; v.y += ay; }
-    }
-    return v;
+    return make_int2(wave_inclusive_scan(v.x), wave_inclusive_scan(v.y));
 }
 
 // Exclusive prefix sum of an int pair across a workgroup of WAVES waves, in
@@ -177,6 +187,90 @@ __device__ __forceinline__ int2 block_exclusive_scan2(int2 v, int2 *s_tmp, int2 
     __syncthreads();
     total = all;
     return make_int2(before.x + inc.x - v.x, before.y + inc.y - v.y);
+}
+
+// This lane's J entries of the wave's J*64 consecutive ones from `base`
+// (expert ids; entries past N read as 0 and are masked later).  Issued before
+// the workgroup clears its counters, so the load latency overlaps that work.
+template <int J>
+__device__ __forceinline__ void load_keys(const int32_t *__restrict__ idx, int N, int base, int (&raw)[J]) {
+    const int lane = threadIdx.x & (kWave - 1);
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+        const int i = base + j * kWave + lane;
+        raw[j] = i < N ? idx[i] : 0;
+    }
+}
+
+// Ranks the wave's J*64 entries from `base` (raw = load_keys' values).  s_wcnt
+// is the wave's [E] counter row (zero on entry; the wave's per-expert totals
+// on exit).  key[j] = expert id or -1 (absent / out of range); local[j] =
+// number of this wave's earlier entries with the same expert.
+template <int J>
+__device__ __forceinline__ void wave_rank(const int (&raw)[J], int N, int E, int nbits, int base,
+                                          unsigned short *s_wcnt, int (&key)[J], int (&local)[J],
+                                          int &flags) {
+    const int lane = threadIdx.x & (kWave - 1);
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+        const int i = base + j * kWave + lane;
+        const bool in = i < N;
+        const int e = raw[j];
+        const bool ok = in && e >= 0 && e < E;
+        if (in && !ok) flags |= FLAG_BAD_EXPERT;
+        const uint64_t m = match_key(e, ok, nbits);
+        const int r = lanes_below(m);
+        const int before = ok ? static_cast<int>(s_wcnt[e]) : 0;
+        // every lane of the group has read the counter; the lowest one advances it
+        if (ok && r == 0) s_wcnt[e] = static_cast<unsigned short>(before + __popcll(m));
+        key[j] = ok ? e : -1;
+        local[j] = before + r;
+    }
+}
+
+// Per-wave counters of expert e -> exclusive prefixes over waves; returns the
+// workgroup's total for e.
+__device__ __forceinline__ int column_scan(unsigned short *s_cnt, int E, int e) {
+    int run = 0;
+#pragma unroll
+    for (int w = 0; w < kLayoutWaves; ++w) {
+        const int c = s_cnt[w * E + e];
+        s_cnt[w * E + e] = static_cast<unsigned short>(run);
+        run += c;
+    }
+    return run;
+}
+
+// Entries of every 1024-entry tile except tile `b` (of nblk), counted per
+// expert into s_before (tiles before b) and s_after (tiles after b) with LDS
+// atomics; entries with an expert outside [0,E) set FLAG_BAD_EXPERT in flags
+// and are added to bad.  16 loads in flight per thread.  Redundant work that
+// lets one workgroup per tile know every count without talking to the others.
+__device__ __forceinline__ void count_other_tiles(const int32_t *__restrict__ idx, int N, int E, int nblk,
+                                                  int b, int *s_before, int *s_after, int &flags, int &bad) {
+    const int tid = threadIdx.x;
+    constexpr int kBatch = 16;
+    for (int t0 = 0; t0 < nblk; t0 += kBatch) {
+        int ev[kBatch];
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+            const int t = t0 + u, i = t * kLayoutThreads + tid;
+            ev[u] = (t < nblk && t != b && i < N) ? idx[i] : 0;
+        }
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+            const int t = t0 + u, i = t * kLayoutThreads + tid;
+            if (t < nblk && t != b && i < N) {
+                const int e = ev[u];
+                if (e >= 0 && e < E) {
+                    atomicAdd(t < b ? &s_before[e] : &s_after[e], 1);
+                } else {
+                    flags |= FLAG_BAD_EXPERT;
+                    ++bad;
+                }
+            }
+        }
+    }
 }
 
 }  // namespace moe

@@ -193,7 +193,9 @@ moe_status moe_combine(const moe_layout_desc *desc, const moe_layout_bufs *layou
  *              segments per rank = its E/R experts then its B slots;
  *              slot_expert [R*B]: expert copied in each slot, -1 if unused
  *              (the weights a rank must hold in that slot).
- *   workspace  at least moe_layout_balanced_workspace_bytes, 256-byte aligned.
+ *   workspace  at least moe_layout_balanced_workspace_bytes, 256-byte aligned;
+ *              that is 0 for S*K <= 32768 (one launch, no scratch), and
+ *              workspace may then be NULL.
  * pos/src are ordinary maps, so moe_dispatch and moe_combine take this
  * layout unchanged. */
 enum { MOE_FLAG_UNBALANCED = 4 };

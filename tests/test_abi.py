@@ -120,6 +120,23 @@ def test_dispatch_combine_argument_errors(moe):
     assert lib.moe_combine(ctypes.byref(e), ctypes.byref(b), None, 256, None, None, None, None) == moe.MOE_OK
 
 
+def test_balanced_workspace_rule(moe):
+    """The balanced layout needs no scratch up to 32K entries (one launch) and
+    reports MOE_ERR_WORKSPACE above that when none is given.  No launch."""
+    assert moe.moe_layout_balanced_workspace_bytes(moe.LayoutDesc(4096, 8, 256, 8), 16) == 0
+    big = moe.LayoutDesc(4097, 8, 256, 8)
+    need = moe.moe_layout_balanced_workspace_bytes(big, 16)
+    assert need >= 2 * 4097 * 8 * 4          # the plain layout's pos and src
+    lib = moe.lib()
+    P = ctypes.c_void_p
+    d, b = big.c(), _bufs(moe)
+    bb = moe.moe_balance_bufs(FAKE, FAKE + (1 << 16))
+    args = (ctypes.byref(d), 16, P(FAKE), ctypes.byref(b), ctypes.byref(bb))
+    assert lib.moe_layout_balanced(*args, None, 0, None) == moe.MOE_ERR_WORKSPACE
+    assert lib.moe_layout_balanced(*args, P(FAKE), need - 256, None) == moe.MOE_ERR_WORKSPACE
+    assert lib.moe_layout_balanced(*args, P(FAKE + 16), need, None) == moe.MOE_ERR_ALIGN
+
+
 def test_status_strings(moe):
     for s in range(6):
         assert moe.moe_status_str(s).startswith("MOE_")

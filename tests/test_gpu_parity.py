@@ -465,6 +465,7 @@ BAL = [
     ("no-slots", 700, 3, 24, 4, 0, "pow"),
     ("E1024-R8-B64", 2000, 8, 1024, 8, 64, "pow"),
     ("big-N100000-E96-R6", 12500, 8, 96, 6, 8, "pow"),
+    ("big-bad-ids-N40000", 5000, 8, 64, 8, 4, "bad"),     # two-step path with invalid ids
     ("empty", 0, 4, 16, 4, 2, "pow"),
 ]
 
