@@ -339,6 +339,8 @@ def main(argv=None):
     ap.add_argument("--calib-copy", action="store_true")
     ap.add_argument("--only-decode", action="store_true",
                     help="time only the decode call (S=128) and print its JSON object")
+    ap.add_argument("--only-balanced", action="store_true",
+                    help="time only the balanced layout on the skew batch and print its JSON object")
     args = ap.parse_args(argv)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -356,6 +358,9 @@ def main(argv=None):
     dev = torch.device("cuda:0")
     if args.only_decode:
         print(json.dumps(decode_numbers(moe, CONFIGS["decode"], dev, args.decode_iters)), flush=True)
+        return
+    if args.only_balanced:
+        print(json.dumps(balanced_numbers(moe, CONFIGS["skew"], dev)), flush=True)
         return
     cfg = CONFIGS[args.config]
     run = Run(moe, cfg, dev)
