@@ -149,23 +149,37 @@ __device__ __forceinline__ void token_experts(const LayoutArgs &a, int t, int (&
 template <int K>
 __device__ __forceinline__ void token_rows(const LayoutArgs &a, const int (&e)[K], const SmallLayoutLds &L,
                                            int (&p)[K]) {
+    // all 2K LDS reads first (an invalid id reads expert 0 and is dropped
+    // below), so they are in flight together instead of one after another
+    int pre[K], off[K];
 #pragma unroll
     for (int k = 0; k < K; ++k) {
-        int row = -1;
-        if (e[k] >= 0 && e[k] < a.E) {
-            int within = L.pre[e[k]];
+        const int ek = (e[k] >= 0 && e[k] < a.E) ? e[k] : 0;
+        pre[k] = L.pre[ek];
+        off[k] = L.off[ek];
+    }
 #pragma unroll
-            for (int j = 0; j < k; ++j) within += (e[j] == e[k]) ? 1 : 0;
-            if (!(a.pad_mode == PAD_CAPACITY && within >= a.pad_rows)) row = L.off[e[k]] + within;
-        }
-        p[k] = row;
+    for (int k = 0; k < K; ++k) {
+        int within = pre[k];
+#pragma unroll
+        for (int j = 0; j < k; ++j) within += (e[j] == e[k]) ? 1 : 0;
+        const bool placed = e[k] >= 0 && e[k] < a.E && !(a.pad_mode == PAD_CAPACITY && within >= a.pad_rows);
+        p[k] = placed ? off[k] + within : -1;
     }
 }
 
-// pos, src and recv_w of token t's entries (chunk 0 only).
+// Route weight of token t's entry threadIdx.x (threads below K of chunk 0,
+// when recv_w is wanted), loaded at kernel entry with the other inputs.
+template <int K>
+__device__ __forceinline__ float token_weight(const DispatchArgs &da, int t, int c) {
+    const bool mine = c == 0 && threadIdx.x < K && da.recv_w != nullptr && da.topk_w != nullptr;
+    return mine ? da.topk_w[static_cast<size_t>(t) * K + threadIdx.x] : 0.0f;
+}
+
+// pos, src and recv_w of token t's entries (chunk 0 only); w = token_weight.
 template <int K>
 __device__ __forceinline__ void write_token_maps(const LayoutArgs &la, const DispatchArgs &da, int t,
-                                                 const int (&p)[K]) {
+                                                 const int (&p)[K], float w) {
 #pragma unroll
     for (int k = 0; k < K; ++k) {
         if (threadIdx.x == k) {
@@ -173,7 +187,7 @@ __device__ __forceinline__ void write_token_maps(const LayoutArgs &la, const Dis
             la.pos[i] = p[k];
             if (p[k] >= 0) {
                 la.src[p[k]] = i;
-                if (da.recv_w != nullptr && da.topk_w != nullptr) da.recv_w[p[k]] = da.topk_w[i];
+                if (da.recv_w != nullptr && da.topk_w != nullptr) da.recv_w[p[k]] = w;
             }
         }
     }
@@ -195,11 +209,12 @@ __global__ __launch_bounds__(kT) void k_layout_dispatch_fp8(LayoutArgs la, Dispa
     int ev[kPerThread], e[K];
     load_routing(la, ev);
     token_experts<K>(la, t, e);
+    const float w = token_weight<K>(da, t, c);
     if (threadIdx.x == 0) L.flags = 0;
     const int flags = small_layout(la, t, K, ev, L);
     int p[K];
     token_rows<K>(la, e, L, p);
-    if (c == 0) write_token_maps<K>(la, da, t, p);
+    if (c == 0) write_token_maps<K>(la, da, t, p, w);
 
     float scale;
     const u32x4 q = quantize16_e4m3(lo, hi, scale);
@@ -232,11 +247,12 @@ __global__ __launch_bounds__(kT) void k_layout_dispatch_bf16(LayoutArgs la, Disp
     int ev[kPerThread], e[K];
     load_routing(la, ev);
     token_experts<K>(la, t, e);
+    const float w = token_weight<K>(da, t, c);
     if (threadIdx.x == 0) L.flags = 0;
     const int flags = small_layout(la, t, K, ev, L);
     int p[K];
     token_rows<K>(la, e, L, p);
-    if (c == 0) write_token_maps<K>(la, da, t, p);
+    if (c == 0) write_token_maps<K>(la, da, t, p, w);
 
     u32x4 *__restrict__ recv = static_cast<u32x4 *>(da.recv);
     if (active) {
