@@ -9,14 +9,20 @@ scales, bf16 combine).  Prints one JSON line.
 
 Timing: W untimed warm-up steps, then K timed steps bracketed by
 torch.cuda.synchronize(); HIP events on the launch stream around every call
-give per-kernel averages.  Bytes are the algorithmic bytes the path must move
-(padding rows excluded), GB = 1e9.
+give per-kernel averages.  A percentile pass adds p10 / median / p90 per call
+over 100 iterations (1000 for the decode call), back to back ("warm") and
+after overwriting 512 MiB, twice the Infinity Cache ("cold").  Bytes are the
+algorithmic bytes the path must move (padding rows excluded), GB = 1e9.
+Beside the prefill batch the same-shape skewed batch (bf16 dispatch, segments
+padded to 128 rows) is timed too.
 
   --gpus N           only N=1 exists: the EP ranks are partitions of one buffer
   --config NAME      tiny | prefill | decode | skew | dsmoe16b
   --calib-copy       run only a plain device copy of known size (for scaling
                      rocprofv3 FETCH_SIZE / WRITE_SIZE counters)
   --no-cpu-baseline  skip timing the CPU oracle
+  --no-decode        skip the decode, balanced-layout and skewed-batch numbers
+  --no-percentiles   skip the percentile pass
 """
 from __future__ import annotations
 
@@ -186,6 +192,64 @@ def time_steps(run, steps: int, warmup: int):
     return dict(layout_ms=lay, dispatch_ms=dis, combine_ms=com, step_ms=step_ms, wall_s=wall)
 
 
+def call_percentiles(calls, names, iters: int, flush_bytes: int = 0):
+    """p10 / median / p90 (µs) of each call over `iters` iterations, HIP events
+    on the launch stream around every call.  With flush_bytes, every iteration
+    first overwrites a scratch buffer of that size (twice the 256 MB
+    Infinity Cache for 512 MiB) outside the event pairs: cold-cache timing."""
+    import numpy as np
+    import torch
+    scratch = torch.empty(flush_bytes, dtype=torch.uint8, device="cuda") if flush_bytes else None
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)] for _ in range(iters)]
+    for i in range(iters):
+        if scratch is not None:
+            scratch.fill_(i & 0xFF)
+        ev[i][0].record()
+        for j, call in enumerate(calls):
+            call()
+            ev[i][j + 1].record()
+    torch.cuda.synchronize()
+    out = {}
+    for j, name in enumerate(names):
+        us = np.array([ev[i][j].elapsed_time(ev[i][j + 1]) * 1e3 for i in range(iters)])
+        out[name] = [round(float(x), 2) for x in np.percentile(us, [10, 50, 90])]
+    del scratch
+    return out
+
+
+def percentile_numbers(run, drun, iters: int = 100, decode_iters: int = 1000):
+    """Per-call p10 / median / p90 of the step's kernels, warm (back to back)
+    and cold (after a 512 MiB overwrite), at the batch shape and at decode."""
+    big = {"calls": ["layout", "dispatch", "combine"], "iters": iters}
+    calls = (run.layout_call, run.dispatch_call, run.combine_call)
+    big["warm_us"] = call_percentiles(calls, big["calls"], iters)
+    big["cold_us"] = call_percentiles(calls, big["calls"], iters, 512 << 20)
+    res = {"unit": "us [p10, p50, p90]", "batch": big}
+    if drun is not None:
+        dec = {"calls": ["layout_dispatch", "combine"], "iters": decode_iters}
+        dcalls = (drun.layout_dispatch_call, drun.combine_call)
+        dec["warm_us"] = call_percentiles(dcalls, dec["calls"], decode_iters)
+        dec["cold_us"] = call_percentiles(dcalls, dec["calls"], decode_iters, 512 << 20)
+        res["decode"] = dec
+    return res
+
+
+def shape_numbers(moe, cfg, dev, steps: int = 30, warmup: int = 5):
+    """Dispatch + combine GB/s and % of peak of another workload (the skewed
+    batch has the metric's shape with bf16 dispatch and padding)."""
+    r = Run(moe, cfg, dev)
+    _, db, cb = r.bytes()
+    t = time_steps(r, steps, warmup)
+    dc = (db + cb) / ((t["dispatch_ms"] + t["combine_ms"]) * 1e-3) / 1e9
+    out = {"workload": cfg.name, "fp8_dispatch": cfg.fp8, "pad_mode": cfg.pad_mode, "pad_rows": cfg.pad_rows,
+           "dispatch_us": round(t["dispatch_ms"] * 1e3, 2), "combine_us": round(t["combine_ms"] * 1e3, 2),
+           "layout_us": round(t["layout_ms"] * 1e3, 2), "dispatch_plus_combine_gbps": round(dc, 1),
+           "dispatch_plus_combine_frac_of_peak": round(dc / HBM_PEAK_GBPS, 4),
+           "bytes": {"dispatch": db, "combine": cb}}
+    del r
+    return out
+
+
 def time_graph(step, iters: int):
     """One step captured once in a HIP graph, replayed `iters` times."""
     import torch
@@ -225,10 +289,10 @@ def time_calls(step, iters: int, warmup: int = 20):
     return a.elapsed_time(b) / iters
 
 
-def decode_numbers(moe, dcfg, dev, iters: int):
+def decode_numbers(moe, dcfg, dev, iters: int, drun=None):
     """µs per decode call (S=128): moe_layout_dispatch (one launch) + moe_combine,
     eager and graph-replayed, and the three-call variant."""
-    drun = Run(moe, dcfg, dev)
+    drun = drun if drun is not None else Run(moe, dcfg, dev)
     dt = time_steps(drun, iters, 20)
     fused_ms = time_calls(drun.fused_step, iters)
     ld_ms = time_calls(drun.layout_dispatch_call, iters)
@@ -293,6 +357,10 @@ def cpu_baseline(cfg, budget_s: float = 12.0):
     w = make_workload(cfg)
     rows = oracle.max_recv_rows(cfg.S, cfg.K, cfg.E, cfg.R, cfg.pad_mode, cfg.pad_rows)
     y = random_expert_out_bits(w.seed, rows, cfg.H)
+    # one core: the oracle is single-threaded; pin it so the figure is per core
+    old_aff = os.sched_getaffinity(0) if hasattr(os, "sched_getaffinity") else None
+    if old_aff:
+        os.sched_setaffinity(0, {min(old_aff)})
     passes, t_total, nbytes = 0, 0.0, 0
     while t_total < budget_s or passes == 0:
         t0 = time.perf_counter()
@@ -308,10 +376,24 @@ def cpu_baseline(cfg, budget_s: float = 12.0):
         nbytes += (layout_bytes(cfg.S, cfg.K, rows) + dispatch_bytes(cfg.S, cfg.K, cfg.H, cfg.fp8, placed)
                    + combine_bytes(cfg.S, cfg.K, cfg.H, placed, cfg.shared))
         del lo
+    if old_aff:
+        os.sched_setaffinity(0, old_aff)
     return {"value": round(nbytes / t_total / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
             "sample": f"{passes} full {cfg.name} batches (S={cfg.S}, layout + "
                       f"{'fp8' if cfg.fp8 else 'bf16'} dispatch + combine), {t_total:.1f} s single-threaded",
-            "ms_per_step": round(1e3 * t_total / passes, 2), "host_cpus": os.cpu_count()}
+            "ms_per_step": round(1e3 * t_total / passes, 2), "host_cpus": os.cpu_count(),
+            "cpu_model": cpu_model(), "pinned_core": min(old_aff) if old_aff else None}
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def calib_copy(nbytes: int = 1 << 30):
@@ -339,6 +421,8 @@ def main(argv=None):
     ap.add_argument("--calib-copy", action="store_true")
     ap.add_argument("--only-decode", action="store_true",
                     help="time only the decode call (S=128) and print its JSON object")
+    ap.add_argument("--no-percentiles", action="store_true",
+                    help="skip the per-call p10/p50/p90 pass (warm and after a 512 MiB cache flush)")
     ap.add_argument("--only-balanced", action="store_true",
                     help="time only the balanced layout on the skew batch and print its JSON object")
     args = ap.parse_args(argv)
@@ -388,7 +472,12 @@ def main(argv=None):
              "dispatch_plus_combine_frac_of_peak": round(dc_gbps / HBM_PEAK_GBPS, 4),
              "bytes": {"layout": lb, "dispatch": db, "combine": cb}, "wall_s_timed": round(t["wall_s"], 3)}
 
-    decode = None if args.no_decode else decode_numbers(moe, CONFIGS["decode"], dev, args.decode_iters)
+    drun = None if args.no_decode else Run(moe, CONFIGS["decode"], dev)
+    decode = None if args.no_decode else decode_numbers(moe, CONFIGS["decode"], dev, args.decode_iters, drun)
+    pct = None if args.no_percentiles else percentile_numbers(run, drun)
+    also = None
+    if not args.no_decode and cfg.name == "prefill":
+        also = shape_numbers(moe, CONFIGS["skew"], dev)
     balanced = None if args.no_decode else balanced_numbers(moe, CONFIGS["skew"], dev)
     budgets = [int(x) for x in args.cu_budgets.split(",") if x.strip()]
     cu_budget = cu_budget_numbers(moe, run, budgets) if budgets else None
@@ -405,7 +494,7 @@ def main(argv=None):
                    "fp8_dispatch": cfg.fp8, "routing": cfg.routing, "pad_mode": cfg.pad_mode,
                    "pad_rows": cfg.pad_rows, "shared": cfg.shared, "parallelism": f"ep{cfg.R} simulated on 1 GPU"},
         "roofline": roofline, "cpu_baseline": cpu, "kernels": extra, "decode": decode,
-        "cu_budget": cu_budget, "balanced_layout": balanced,
+        "cu_budget": cu_budget, "balanced_layout": balanced, "percentiles": pct, "same_shape_skew": also,
     }
     print(json.dumps(line), flush=True)
 
