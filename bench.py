@@ -22,7 +22,7 @@ padded to 128 rows) is timed too.
                      rocprofv3 FETCH_SIZE / WRITE_SIZE counters)
   --no-cpu-baseline  skip timing the CPU oracle
   --no-decode        skip the decode, balanced-layout and skewed-batch numbers
-  --no-percentiles   skip the percentile pass
+  --no-percentiles   skip the percentile pass and the streaming reference
 """
 from __future__ import annotations
 
@@ -250,6 +250,20 @@ def shape_numbers(moe, cfg, dev, steps: int = 30, warmup: int = 5):
     return out
 
 
+def streaming_reference(cfg, dev, iters: int = 50):
+    """What a plain streaming kernel reaches at combine's byte mix on this GPU
+    in this process: torch.sum over K contiguous bf16 planes of S*H into one
+    (the same bytes in and out as combine, with no gather)."""
+    import torch
+    x = torch.empty((cfg.K, cfg.S * cfg.H), dtype=torch.bfloat16, device=dev).normal_()
+    out = torch.empty(cfg.S * cfg.H, dtype=torch.bfloat16, device=dev)
+    ms = time_calls(lambda: torch.sum(x, dim=0, out=out), iters, 10)
+    nbytes = (cfg.K + 1) * cfg.S * cfg.H * 2
+    del x, out
+    return {"what": f"torch.sum of {cfg.K} contiguous bf16 planes [{cfg.S}x{cfg.H}] into one (same bytes as "
+                    "combine, no gather)", "gbps": round(nbytes / (ms * 1e-3) / 1e9, 1)}
+
+
 def time_graph(step, iters: int):
     """One step captured once in a HIP graph, replayed `iters` times."""
     import torch
@@ -422,7 +436,8 @@ def main(argv=None):
     ap.add_argument("--only-decode", action="store_true",
                     help="time only the decode call (S=128) and print its JSON object")
     ap.add_argument("--no-percentiles", action="store_true",
-                    help="skip the per-call p10/p50/p90 pass (warm and after a 512 MiB cache flush)")
+                    help="skip the per-call p10/p50/p90 pass (warm and after a 512 MiB cache flush) "
+                         "and the streaming reference")
     ap.add_argument("--only-balanced", action="store_true",
                     help="time only the balanced layout on the skew batch and print its JSON object")
     args = ap.parse_args(argv)
@@ -465,6 +480,10 @@ def main(argv=None):
                 "traffic_unit": "HBM bytes per launch",
                 "kernel": dom, "algorithmic_bytes_per_launch": dom_bytes,
                 "avg_launch_us": round(dom_ms * 1e3, 2)}
+    if dom == "combine" and not args.no_percentiles:
+        ref = streaming_reference(cfg, dev)
+        ref["kernel_over_reference"] = round(achieved / ref["gbps"], 3)
+        roofline["streaming_reference"] = ref
 
     extra = {"layout_us": round(t["layout_ms"] * 1e3, 2), "dispatch_us": round(t["dispatch_ms"] * 1e3, 2),
              "combine_us": round(t["combine_ms"] * 1e3, 2), "dispatch_gbps": round(d_gbps, 1),
