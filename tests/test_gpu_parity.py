@@ -303,6 +303,38 @@ def test_buffer_api(moe):
         assert_combine_matches(host_bits(out), oracle.combine(y, ref.pos, w.topk_w), "buffer combine")
 
 
+@pytest.mark.parametrize("name", ["prefill", "skew"])
+def test_bench_step(moe, name):
+    """The exact sequence bench.py times (its Run: static Buffer, prepared
+    layout, dispatch and combine calls without argument checks) at full size:
+    every output against the oracle, combine over the bench's own expert
+    outputs."""
+    import bench
+    cfg = CONFIGS[name]
+    say(f"case bench-step {name}")
+    run = bench.Run(moe, cfg, torch.device(DEV))
+    run.buf.recv.zero_()
+    run.step()
+    torch.cuda.synchronize()
+    w = run.w
+    ref = oracle.layout(w.topk_idx, cfg.E, cfg.R, cfg.pad_mode, cfg.pad_rows)
+    compare_layout(run.buf.layout, ref, f"bench {name} layout")
+    rows = len(ref.src)
+    valid = ref.src >= 0
+    if cfg.fp8:
+        rc, rs, rw = oracle.dispatch_fp8(w.hidden, ref.pos, rows, w.topk_w)
+        assert np.array_equal(run.buf.recv.cpu().numpy()[valid], rc[valid]), "fp8 codes"
+        assert np.array_equal(run.buf.recv_scales.cpu().numpy()[valid].view(np.uint32),
+                              rs[valid].view(np.uint32)), "fp8 scales"
+    else:
+        rb, rw = oracle.dispatch_bf16(w.hidden, ref.pos, rows, w.topk_w)
+        assert np.array_equal(host_bits(run.buf.recv)[valid], rb[valid]), "bf16 rows"
+    assert np.array_equal(run.buf.recv_w.cpu().numpy()[valid].view(np.uint32), rw[valid].view(np.uint32))
+    y = host_bits(run.expert_out)
+    assert_combine_matches(host_bits(run.buf.out), oracle.combine(y, ref.pos, w.topk_w, w.shared),
+                           f"bench {name} combine")
+
+
 def test_graph_replay(moe):
     """Layout + dispatch + combine captured once in a HIP graph and replayed on
     three different batches, with eager work between the replays: every replay
