@@ -335,13 +335,15 @@ def test_bench_step(moe, name):
                            f"bench {name} combine")
 
 
-def test_graph_replay(moe):
+@pytest.mark.parametrize("form", ["three-calls", "fused"])
+def test_graph_replay(moe, form):
     """Layout + dispatch + combine captured once in a HIP graph and replayed on
     three different batches, with eager work between the replays: every replay
     matches the eager result for its batch (no memset nodes are recorded: the
-    layout kernels write every output they own)."""
+    layout kernels write every output they own).  Both forms of the decode
+    call: three calls, and moe_layout_dispatch (one launch) + combine."""
     cfg = CONFIGS["decode"]
-    say("case graph-replay decode")
+    say(f"case graph-replay decode {form}")
     buf = moe.Buffer(cfg.S, cfg.H, cfg.K, cfg.E, cfg.R, fp8=True, pad_mode=cfg.pad_mode,
                      pad_rows=cfg.pad_rows, device=DEV)
     idx = torch.empty((cfg.S, cfg.K), dtype=torch.int32, device=DEV)
@@ -356,8 +358,11 @@ def test_graph_replay(moe):
         tw.copy_(torch.from_numpy(w.topk_w))
 
     def step():
-        buf.layout_call(idx, check=False)
-        buf.dispatch_call(hid, idx, tw, check=False)
+        if form == "fused":
+            buf.layout_dispatch_call(hid, idx, tw, check=False)
+        else:
+            buf.layout_call(idx, check=False)
+            buf.dispatch_call(hid, idx, tw, check=False)
         buf.combine_call(y, tw, check=False)
 
     def snapshot():
@@ -392,6 +397,52 @@ def test_graph_replay(moe):
         torch.cuda.synchronize()
         got = snapshot()
         for a, b in zip(got, want):
+            assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("S", [2000, 5000], ids=["one-launch-N16000", "two-step-N40000"])
+def test_graph_replay_balanced(moe, S):
+    """The balanced layout captured in a HIP graph and replayed on three
+    batches: every replay equals the eager call for that batch."""
+    K, E, R, B = 8, 64, 8, 4
+    say(f"case graph-replay balanced S={S}")
+    desc = moe.LayoutDesc(S, K, E, R)
+    lay = moe.alloc_layout(desc, DEV)
+    bal = moe.alloc_balance(desc, B, DEV)
+    idx = torch.empty((S, K), dtype=torch.int32, device=DEV)
+    cfg = _case("graph-bal", S, 8, E, K, R, routing="zipf")
+
+    def step():
+        moe.moe_layout_balanced(desc, B, idx, lay, bal)
+
+    def snapshot():
+        return [t.clone() for t in (lay.pos, lay.src, lay.expert_offset, lay.tokens_per_rank, lay.status,
+                                    bal.seg_offset, bal.slot_expert)]
+
+    idx.copy_(torch.from_numpy(make_workload(cfg, seed=1, with_hidden=False).topk_idx))
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    torch.cuda.synchronize()
+    for seed in (21, 22, 23):
+        idx.copy_(torch.from_numpy(make_workload(cfg, seed=seed, with_hidden=False).topk_idx))
+        for t in (lay.pos, lay.src):
+            t.fill_(-7)
+        step()
+        torch.cuda.synchronize()
+        want = snapshot()
+        for t in (lay.pos, lay.src):
+            t.fill_(-7)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for a, b in zip(snapshot(), want):
             assert torch.equal(a, b)
 
 
