@@ -217,9 +217,10 @@ def call_percentiles(calls, names, iters: int, flush_bytes: int = 0):
     return out
 
 
-def percentile_numbers(run, drun, iters: int = 100, decode_iters: int = 1000):
+def percentile_numbers(run, drun, iters: int = 100, decode_iters: int = 1000, trun=None):
     """Per-call p10 / median / p90 of the step's kernels, warm (back to back)
-    and cold (after a 512 MiB overwrite), at the batch shape and at decode."""
+    and cold (after a 512 MiB overwrite), at the batch shape, at decode and
+    for the tiny batch (cache-resident: no roofline claim)."""
     big = {"calls": ["layout", "dispatch", "combine"], "iters": iters}
     calls = (run.layout_call, run.dispatch_call, run.combine_call)
     big["warm_us"] = call_percentiles(calls, big["calls"], iters)
@@ -231,6 +232,12 @@ def percentile_numbers(run, drun, iters: int = 100, decode_iters: int = 1000):
         dec["warm_us"] = call_percentiles(dcalls, dec["calls"], decode_iters)
         dec["cold_us"] = call_percentiles(dcalls, dec["calls"], decode_iters, 512 << 20)
         res["decode"] = dec
+    if trun is not None:
+        tiny = {"calls": big["calls"], "iters": decode_iters}
+        tcalls = (trun.layout_call, trun.dispatch_call, trun.combine_call)
+        tiny["warm_us"] = call_percentiles(tcalls, tiny["calls"], decode_iters)
+        tiny["cold_us"] = call_percentiles(tcalls, tiny["calls"], decode_iters, 512 << 20)
+        res["tiny"] = tiny
     return res
 
 
@@ -381,7 +388,7 @@ def cpu_baseline(cfg, budget_s: float = 12.0):
     old_aff = os.sched_getaffinity(0) if hasattr(os, "sched_getaffinity") else None
     if old_aff:
         os.sched_setaffinity(0, {min(old_aff)})
-    passes, t_total, nbytes = 0, 0.0, 0
+    passes, t_total, nbytes, times = 0, 0.0, 0, []
     while t_total < budget_s or passes == 0:
         t0 = time.perf_counter()
         lo = oracle.layout(w.topk_idx, cfg.E, cfg.R, cfg.pad_mode, cfg.pad_rows)
@@ -390,7 +397,8 @@ def cpu_baseline(cfg, budget_s: float = 12.0):
         else:
             oracle.dispatch_bf16(w.hidden, lo.pos, rows, w.topk_w)
         oracle.combine(y, lo.pos, w.topk_w, w.shared)
-        t_total += time.perf_counter() - t0
+        times.append(time.perf_counter() - t0)
+        t_total += times[-1]
         passes += 1
         placed = int(lo.tokens_per_expert.sum())
         nbytes += (layout_bytes(cfg.S, cfg.K, rows) + dispatch_bytes(cfg.S, cfg.K, cfg.H, cfg.fp8, placed)
@@ -401,7 +409,8 @@ def cpu_baseline(cfg, budget_s: float = 12.0):
     return {"value": round(nbytes / t_total / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
             "sample": f"{passes} full {cfg.name} batches (S={cfg.S}, layout + "
                       f"{'fp8' if cfg.fp8 else 'bf16'} dispatch + combine), {t_total:.1f} s single-threaded",
-            "ms_per_step": round(1e3 * t_total / passes, 2), "host_cpus": os.cpu_count(),
+            "ms_per_step": round(1e3 * t_total / passes, 2),
+            "ms_per_step_median": round(1e3 * float(np.median(times)), 2), "host_cpus": os.cpu_count(),
             "cpu_model": cpu_model(), "pinned_core": min(old_aff) if old_aff else None}
 
 
@@ -499,7 +508,8 @@ def main(argv=None):
 
     drun = None if args.no_decode else Run(moe, CONFIGS["decode"], dev)
     decode = None if args.no_decode else decode_numbers(moe, CONFIGS["decode"], dev, args.decode_iters, drun)
-    pct = None if args.no_percentiles else percentile_numbers(run, drun)
+    pct = None if args.no_percentiles else percentile_numbers(
+        run, drun, trun=None if args.no_decode else Run(moe, CONFIGS["tiny"], dev))
     also = None
     if not args.no_decode and cfg.name == "prefill":
         also = shape_numbers(moe, CONFIGS["skew"], dev)
