@@ -112,9 +112,10 @@ typedef struct {
  * Host only.  Returns -1 if the shape is invalid. */
 int64_t moe_max_recv_rows(const moe_layout_desc *desc);
 
-/* Device workspace bytes moe_layout needs for this shape (0 when
- * S*K <= 32768: those batches run as one launch with no scratch).  Host only.  Returns 0 for an invalid shape too; moe_layout then
- * reports MOE_ERR_SHAPE. */
+/* Device workspace bytes moe_layout needs for this shape: 0 when
+ * S*K <= 32768 (those batches run as one launch with no scratch), else one
+ * histogram of E counts per tile.  Host only.  Returns 0 for an invalid shape
+ * too; moe_layout then reports MOE_ERR_SHAPE. */
 size_t moe_layout_workspace_bytes(const moe_layout_desc *desc);
 
 /* Layout of one batch from its top-k routing.
