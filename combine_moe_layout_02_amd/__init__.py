@@ -371,10 +371,19 @@ class Buffer:
     returns the token-order result.  Every call is asynchronous on the current
     stream (or the one given); outputs are views of the buffer's own tensors
     and are overwritten by the next call.
+
+    With ``balance_slots=B`` the layout is the balanced one (moe_layout_balanced:
+    every rank receives the same number of rows, the surplus of hot experts
+    going to B replica slots per rank; MoonEP article, section 1); dispatch and
+    combine are unchanged.  ``balance.slot_expert`` then tells which expert each
+    slot must hold.
     """
 
     def __init__(self, S: int, H: int, K: int, E: int, R: int, fp8: bool = False,
-                 pad_mode: int = MOE_PAD_NONE, pad_rows: int = 0, device="cuda", shared: bool = False):
+                 pad_mode: int = MOE_PAD_NONE, pad_rows: int = 0, device="cuda",
+                 balance_slots: Optional[int] = None):
+        if balance_slots is not None and pad_mode != MOE_PAD_NONE:
+            raise MoeError(MOE_ERR_SHAPE, "Buffer: the balanced layout has no padding")
         self.desc = LayoutDesc(S, K, E, R, pad_mode, pad_rows)
         self.rows = moe_max_recv_rows(self.desc)
         if self.rows < 0 or H < 8 or H % 8 or (fp8 and H % 128):
@@ -398,6 +407,13 @@ class Buffer:
         self._scales = _ptr(self.recv_scales)
         self._recv_w = _ptr(self.recv_w)
         self._out = _ptr(self.out)
+        self.balance, self.slots = None, balance_slots
+        if balance_slots is not None:
+            self.balance = alloc_balance(self.desc, balance_slots, dev)
+            self._bal = self.balance.c()
+            self._balp = ctypes.byref(self._bal)
+            bws = self.balance.workspace
+            self._bws = (_ptr(bws), 0 if bws is None else bws.numel())
 
     def _inputs(self, hidden, topk_idx, topk_w):
         S, K = self.desc.S, self.desc.K
@@ -408,6 +424,12 @@ class Buffer:
     def layout_call(self, topk_idx, stream=None, check=True):
         if check:
             _check(topk_idx, "topk_idx", torch.int32, (self.desc.S, self.desc.K), self.device)
+        if self.balance is not None:
+            rc = _lib.moe_layout_balanced(self._dp, self.slots, _ptr(topk_idx), self._bp, self._balp,
+                                          self._bws[0], self._bws[1], _stream(stream, self.device))
+            if rc != MOE_OK:
+                raise MoeError(rc, "moe_layout_balanced")
+            return
         rc = _lib.moe_layout(self._dp, _ptr(topk_idx), self._bp, self._ws[0], self._ws[1],
                              _stream(stream, self.device))
         if rc != MOE_OK:
@@ -423,9 +445,14 @@ class Buffer:
             raise MoeError(rc, "moe_dispatch")
 
     def layout_dispatch_call(self, hidden, topk_idx, topk_w=None, stream=None, check=True):
-        """moe_layout_dispatch: one launch for decode-sized batches."""
+        """moe_layout_dispatch: one launch for decode-sized batches (with a
+        balanced layout: the balanced layout, then moe_dispatch)."""
         if check:
             self._inputs(hidden, topk_idx, topk_w)
+        if self.balance is not None:
+            self.layout_call(topk_idx, stream, check=False)
+            self.dispatch_call(hidden, topk_idx, topk_w, stream, check=False)
+            return
         rc = _lib.moe_layout_dispatch(self._dp, _ptr(topk_idx), self._bp, self._ws[0], self._ws[1], _ptr(hidden),
                                       self.H, _ptr(topk_w), 1 if self.fp8 else 0, self._recv, self._scales,
                                       self._recv_w if topk_w is not None else None, _stream(stream, self.device))

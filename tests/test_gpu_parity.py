@@ -401,6 +401,37 @@ def test_graph_replay(moe, form):
 
 
 @pytest.mark.parametrize("S", [2000, 5000], ids=["one-launch-N16000", "two-step-N40000"])
+def test_buffer_balanced(moe, S):
+    """Buffer with balance_slots: its prepared calls (balanced layout, FP8
+    dispatch, combine) against the oracle, every output bit for bit."""
+    K, E, R, B, H = 8, 64, 8, 4, 256
+    cfg = _case("buffer-balanced", S, H, E, K, R, routing="zipf")
+    w = make_workload(cfg)
+    say(f"case buffer-balanced S={S}")
+    buf = moe.Buffer(S, H, K, E, R, fp8=True, device=DEV, balance_slots=B)
+    idx = torch.from_numpy(w.topk_idx).to(DEV)
+    tw = torch.from_numpy(w.topk_w).to(DEV)
+    recv, recv_w, eoff, scales = buf.dispatch(dev_bf16(w.hidden, DEV), tw, idx)
+    torch.cuda.synchronize()
+    ref = oracle.layout_balanced(w.topk_idx, E, R, B)
+    for k in ("tokens_per_expert", "tokens_per_rank", "expert_offset", "rank_offset", "pos", "src", "status"):
+        want = getattr(ref, k)
+        assert np.array_equal(getattr(buf.layout, k).cpu().numpy().reshape(want.shape), want), k
+    assert np.array_equal(buf.balance.seg_offset.cpu().numpy(), ref.seg_offset)
+    assert np.array_equal(buf.balance.slot_expert.cpu().numpy()[:R * B], ref.slot_expert)
+    assert int((ref.slot_expert >= 0).sum()) > 0, "the batch should need replicas"
+    valid = ref.src >= 0
+    rc, rs, rw = oracle.dispatch_fp8(w.hidden, ref.pos, len(ref.src), w.topk_w)
+    assert np.array_equal(recv.cpu().numpy()[valid], rc[valid])
+    assert np.array_equal(scales.cpu().numpy()[valid].view(np.uint32), rs[valid].view(np.uint32))
+    assert np.array_equal(recv_w.cpu().numpy()[valid].view(np.uint32), rw[valid].view(np.uint32))
+    y = random_expert_out_bits(w.seed, len(ref.src), H, row_mask=valid, poison=POISON_BF16)
+    out = buf.combine(dev_bf16(y, DEV), tw)
+    torch.cuda.synchronize()
+    assert_combine_matches(host_bits(out), oracle.combine(y, ref.pos, w.topk_w), "buffer balanced combine")
+
+
+@pytest.mark.parametrize("S", [2000, 5000], ids=["one-launch-N16000", "two-step-N40000"])
 def test_graph_replay_balanced(moe, S):
     """The balanced layout captured in a HIP graph and replayed on three
     batches: every replay equals the eager call for that batch."""
