@@ -127,6 +127,39 @@ EDGE = [
 ]
 
 
+def _random_shapes(n=40, seed=4242):
+    """Seeded random shapes spanning every layout variant (single workgroup,
+    one launch over tiles, two launches with 1024/2048-entry tiles), both
+    dispatch formats, all pad modes and odd sizes."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        fp8 = bool(rng.integers(0, 2))
+        H = int(rng.integers(1, 9)) * 128 if fp8 else int(rng.integers(1, 97)) * 8
+        R = int(rng.choice([1, 2, 3, 4, 5, 8, 16]))
+        E = R * int(rng.integers(1, max(2, 1024 // R // 4)))
+        K = int(rng.integers(1, min(16, E) + 1))
+        N = int(rng.choice([rng.integers(1, 2049), rng.integers(2049, 32769), rng.integers(32769, 140000)]))
+        S = max(1, N // K)
+        pad = int(rng.integers(0, 3))
+        pad_rows = {PAD_NONE: 0, PAD_MULTIPLE: int(rng.integers(1, 130)),
+                    PAD_CAPACITY: int(max(1, S * K // E * rng.uniform(0.5, 1.5)))}[pad]
+        shared = bool(rng.integers(0, 4) == 0)
+        out.append((_case(f"rand{i}", S, H, E, K, R, pad, pad_rows), fp8, shared))
+    return out
+
+
+RANDOM_SHAPES = _random_shapes()
+
+
+@pytest.mark.parametrize("case", RANDOM_SHAPES, ids=[c[0].name for c in RANDOM_SHAPES])
+def test_random_shapes(moe, case):
+    cfg, fp8, shared = case
+    w = make_workload(cfg, seed=9000 + RANDOM_SHAPES.index(case))
+    sh = make_workload(cfg, seed=9500 + RANDOM_SHAPES.index(case)).hidden if shared else None
+    run_and_check(moe, cfg, w.topk_idx, w.hidden, w.topk_w, shared=sh, fp8=fp8, seed=w.seed)
+
+
 @pytest.mark.parametrize("case", EDGE, ids=[c[0].name for c in EDGE])
 def test_edge_cases(moe, case):
     cfg, fp8, routing, with_shared = case
