@@ -524,6 +524,30 @@ FUSED = [
 ]
 
 
+def _random_fused(n=20, seed=5151):
+    """Seeded random decode-sized shapes for moe_layout_dispatch (most within
+    the one-launch limit S*K <= 4096, some just past it)."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        fp8 = bool(rng.integers(0, 2))
+        H = int(rng.integers(1, 9)) * 128 if fp8 else int(rng.integers(1, 129)) * 8
+        R = int(rng.choice([1, 2, 4, 8]))
+        E = R * int(rng.integers(1, 1024 // R + 1))
+        routing = str(rng.choice(["uniform", "uniform", "dup", "bad"]))
+        K = int(rng.integers(1, min(16, E) + 1)) if routing == "uniform" else int(rng.integers(1, 17))
+        N = int(rng.integers(1, 4097)) if i % 5 else int(rng.integers(4097, 6000))
+        S = max(1, N // K)
+        pad = int(rng.integers(0, 3))
+        pad_rows = {PAD_NONE: 0, PAD_MULTIPLE: int(rng.integers(1, 130)),
+                    PAD_CAPACITY: int(max(1, S * K // E * rng.uniform(0.5, 2.0)))}[pad]
+        out.append((f"rand-fused{i}", S, H, E, K, R, pad, pad_rows, fp8, routing))
+    return out
+
+
+FUSED += _random_fused()
+
+
 @pytest.mark.parametrize("case", FUSED, ids=[c[0] for c in FUSED])
 def test_layout_dispatch(moe, case):
     """moe_layout_dispatch (one launch for S*K <= 4096, two otherwise) against
@@ -615,6 +639,25 @@ BAL = [
     ("big-bad-ids-N40000", 5000, 8, 64, 8, 4, "bad"),     # two-step path with invalid ids
     ("empty", 0, 4, 16, 4, 2, "pow"),
 ]
+
+
+def _random_bal(n=16, seed=6161):
+    """Seeded random balanced-layout shapes, both forms (one launch up to 32K
+    entries, two steps above)."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        R = int(rng.choice([1, 2, 3, 4, 6, 8, 16]))
+        E = R * int(rng.integers(1, 1024 // R + 1))
+        K = int(rng.integers(1, 17))
+        N = int(rng.integers(1, 32769)) if i % 4 else int(rng.integers(32769, 70000))
+        S = max(1, N // K)
+        B = int(rng.integers(0, min(64, 512 // R) + 1))
+        out.append((f"rand-bal{i}", S, K, E, R, B, str(rng.choice(["pow", "pow", "bad"]))))
+    return out
+
+
+BAL += _random_bal()
 
 
 @pytest.mark.parametrize("case", BAL, ids=[c[0] for c in BAL])
