@@ -62,17 +62,43 @@ struct BalanceLds {
     int piece_n[kMaxE];
     int dest_r[kMaxE];        // ranks below their quota, ascending, and their room
     int dest_room[kMaxE];
-    int ndest;
     int rep_e[kMaxBalanceSlots];
     int rep_n[kMaxBalanceSlots];
     int rep_rs[kMaxBalanceSlots];    // (destination rank << 8) | slot
     int slot_rep[kMaxBalanceSlots];  // replica held by (rank, slot), -1 if none
     int mrep[kMaxBalanceSlots];      // parallel merge: replicas before each merged breakpoint
+    int A[kMaxE];             // start of each piece in the shed stream
+    int C[kMaxE];             // start of each destination in the room stream
+    int pre[kMaxE];           // counts in planning order, exclusive prefix
     int seg_off[kMaxE + kMaxBalanceSlots + 1];
     int2 tmp[kLayoutWaves];
-    int npiece;
+    int4 tmp4[kLayoutWaves];
     int flags;
 };
+
+// Exclusive prefix sums of four ints at once across the workgroup, in thread
+// order (the four component scans of one pass share its two barriers).
+// Returns the prefix; `total` gets the workgroup totals.
+__device__ __forceinline__ int4 block_exclusive_scan4(int4 v, int4 *s_tmp, int4 &total) {
+    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+    const int4 inc = make_int4(wave_inclusive_scan(v.x), wave_inclusive_scan(v.y), wave_inclusive_scan(v.z),
+                               wave_inclusive_scan(v.w));
+    if (lane == kWave - 1) s_tmp[wave] = inc;
+    __syncthreads();
+    int4 before = make_int4(0, 0, 0, 0), all = make_int4(0, 0, 0, 0);
+#pragma unroll
+    for (int w = 0; w < kLayoutWaves; ++w) {
+        const int4 t = s_tmp[w];
+        if (w < wave) {
+            before.x += t.x; before.y += t.y; before.z += t.z; before.w += t.w;
+        }
+        all.x += t.x; all.y += t.y; all.z += t.z; all.w += t.w;
+    }
+    __syncthreads();
+    total = all;
+    return make_int4(before.x + inc.x - v.x, before.y + inc.y - v.y, before.z + inc.z - v.z,
+                     before.w + inc.w - v.w);
+}
 
 // The plan, from L.cnt (entries per expert, visible to every thread) and
 // L.flags; valid = entries with an expert in range.  Called by all threads of
@@ -81,6 +107,9 @@ struct BalanceLds {
 __device__ __forceinline__ void plan_balance(BalanceLds &L, int E, int R, int B, int valid) {
     const int tid = threadIdx.x;
     const int epr = E / R, nseg = epr + B, ngrp = R * nseg;
+    // Step 1, from the counts alone: initial results, each rank's room
+    // (quota - load) and each expert's place in its rank's size order (count
+    // descending, id ascending).
     for (int e = tid; e < E; e += kLayoutThreads) {
         L.home[e] = L.cnt[e];
         L.first_rep[e] = 0;
@@ -99,8 +128,6 @@ __device__ __forceinline__ void plan_balance(BalanceLds &L, int E, int R, int B,
         for (; j < epr; ++j) load += L.cnt[r * epr + j];
         L.room[r] = valid / R + (r < valid % R ? 1 : 0) - load;
     }
-    __syncthreads();
-    // each expert's place in its rank's size order (count desc, id asc)
     if (tid < E) {
         const int e = tid, r0 = (e / epr) * epr, c = L.cnt[e];
         int before = 0, j = r0;
@@ -118,63 +145,55 @@ __device__ __forceinline__ void plan_balance(BalanceLds &L, int E, int R, int B,
         L.order[r0 + before] = e;
     }
     __syncthreads();
-    // Entries each expert sheds: its rank's surplus minus the counts of the
-    // rank's larger experts, clamped to [0, count] -- what the sequential plan
-    // takes from it as long as destinations do not run out.  The non-zero
-    // pieces are compacted in planning order (ranks ascending, size order).
-    {
-        // counts in planning order, scanned: larger = prefix - prefix at the rank's start
-        const int c = tid < E ? L.cnt[L.order[tid]] : 0;
-        int2 tot0;
-        const int2 pre = block_exclusive_scan2(make_int2(c, 0), L.tmp, tot0);
-        if (tid < E) L.piece_n[tid] = pre.x;     // scratch: prefix of counts in order
-        __syncthreads();
-        int my = 0;
-        if (tid < E) {
-            const int r = L.order[tid] / epr;
-            const int larger = pre.x - L.piece_n[r * epr];
-            my = -L.room[r] - larger;
-            my = my < 0 ? 0 : (my > c ? c : my);
-        }
-        __syncthreads();
-        int2 total;
-        const int2 ex = block_exclusive_scan2(make_int2(my > 0 ? 1 : 0, 0), L.tmp, total);
-        if (tid < E && my > 0) {
-            L.piece_e[ex.x] = L.order[tid];
-            L.piece_n[ex.x] = my;
-        }
-        if (tid == 0) L.npiece = total.x;
-        // destinations: ranks below their quota, ascending
-        const int room = tid < R ? L.room[tid] : 0;
-        int2 dtot;
-        const int2 dex = block_exclusive_scan2(make_int2(room > 0 ? 1 : 0, 0), L.tmp, dtot);
-        if (tid < R && room > 0) {
-            L.dest_r[dex.x] = tid;
-            L.dest_room[dex.x] = room;
-        }
-        if (tid == 0) L.ndest = B > 0 ? dtot.x : 0;
+
+    // Step 2: entries each expert sheds -- its rank's surplus minus the counts
+    // of the rank's larger experts, clamped to [0, count]: what the sequential
+    // plan takes from it as long as destinations do not run out.  Needs the
+    // counts scanned in planning order (ranks ascending, size order).
+    const int c = tid < E ? L.cnt[L.order[tid]] : 0;
+    int2 tot0;
+    const int2 pre = block_exclusive_scan2(make_int2(c, 0), L.tmp, tot0);
+    if (tid < E) L.pre[tid] = pre.x;
+    __syncthreads();
+    int my = 0;
+    if (tid < E) {
+        const int r = L.order[tid] / epr;
+        my = -L.room[r] - (pre.x - L.pre[r * epr]);
+        my = my < 0 ? 0 : (my > c ? c : my);
     }
+    // Step 3, one scan for four things: the non-zero pieces compacted in
+    // planning order with their starts in the shed stream (A), and the ranks
+    // below their quota (destinations, ascending) with their starts in the
+    // room stream (C).
+    const int room = tid < R ? L.room[tid] : 0;
+    int4 tot4;
+    const int4 ex4 = block_exclusive_scan4(make_int4(my > 0 ? 1 : 0, my, room > 0 ? 1 : 0, room > 0 ? room : 0),
+                                          L.tmp4, tot4);
+    if (my > 0) {
+        L.piece_e[ex4.x] = L.order[tid];
+        L.piece_n[ex4.x] = my;
+        L.A[ex4.x] = ex4.y;
+    }
+    if (room > 0) {
+        L.dest_r[ex4.z] = tid;
+        L.dest_room[ex4.z] = room;
+        L.C[ex4.z] = ex4.w;
+    }
+    const int npiece = tot4.x, T = tot4.y, ndest = B > 0 ? tot4.z : 0;
     __syncthreads();
 
-    // Parallel merge of pieces into destinations.  Laid end to end, the
-    // pieces (planning order) and the destinations' rooms (ascending rank)
-    // both cover [0, T): the overloaded ranks' surpluses add up to the other
-    // ranks' rooms.  A replica is a non-empty overlap of one piece's span with
-    // one destination's span, numbered in stream order -- what the sequential
-    // greedy below produces whenever no destination needs more than B slots.
-    // If one would, or the totals differ, the sequential loop runs instead.
+    // Step 4: merge of pieces into destinations.  Laid end to end, the pieces
+    // and the destinations' rooms both cover [0, T): the overloaded ranks'
+    // surpluses add up to the other ranks' rooms.  A replica is a non-empty
+    // overlap of one piece's span with one destination's span, numbered in
+    // stream order -- what the sequential greedy below produces whenever no
+    // destination needs more than B slots.  If one would, or the totals differ,
+    // the parallel results are undone and the sequential loop runs instead.
     bool merged = false;
-    const int npiece = L.npiece, ndest = L.ndest;
     if (npiece > 0 && ndest > 0 && npiece + ndest <= kMaxBalanceSlots) {  // uniform
-        int2 tot;
-        const int2 ex = block_exclusive_scan2(make_int2(tid < npiece ? L.piece_n[tid] : 0,
-                                                        tid < ndest ? L.dest_room[tid] : 0), L.tmp, tot);
-        int *A = L.order, *C = L.room;  // piece and destination starts (both no longer read)
-        if (tid < npiece) A[tid] = ex.x;
-        if (tid < ndest) C[tid] = ex.y;
-        __syncthreads();
+        const int *A = L.A, *C = L.C;
         // merged breakpoints, ties: piece start first (its interval is then empty)
-        const int M = npiece + ndest, T = tot.x;
+        const int M = npiece + ndest;
         int *mval = L.seg_off;  // scratch until the segment scan
         if (tid < npiece) mval[tid + count_below(C, ndest, A[tid])] = A[tid];
         if (tid < ndest) mval[tid + count_upto(A, npiece, C[tid])] = C[tid];
@@ -184,33 +203,40 @@ __device__ __forceinline__ void plan_balance(BalanceLds &L, int E, int R, int B,
         const int2 rex = block_exclusive_scan2(make_int2(len > 0 ? 1 : 0, 0), L.tmp, rtot);
         if (tid < M) L.mrep[tid] = rex.x;
         __syncthreads();
-        int q = 0, d = 0, slot = 0;
+        bool bad = false;
         if (len > 0) {
-            q = rex.x;
-            d = count_upto(C, ndest, mval[tid]) - 1;                    // destination holding it
-            slot = q - L.mrep[d + count_upto(A, npiece, C[d])];          // its first replica is slot 0
-        }
-        const bool over = __syncthreads_or((len > 0 && slot >= B) || tot.x != tot.y);
-        if (!over) {
-            if (len > 0) {
-                const int pc = count_upto(A, npiece, mval[tid]) - 1;   // piece holding it
+            const int q = rex.x;
+            const int d = count_upto(C, ndest, mval[tid]) - 1;                    // destination holding it
+            const int slot = q - L.mrep[d + count_upto(A, npiece, C[d])];          // its first replica is slot 0
+            if (slot < B) {
+                const int pc = count_upto(A, npiece, mval[tid]) - 1;              // piece holding it
                 const int dr = L.dest_r[d];
                 L.rep_e[q] = L.piece_e[pc];
                 L.rep_n[q] = len;
                 L.rep_rs[q] = (dr << 8) | slot;
                 L.slot_rep[dr * B + slot] = q;
+            } else {
+                bad = true;
             }
-            if (tid < npiece) {
-                const int e = L.piece_e[tid];
-                const int first = L.mrep[tid + count_below(C, ndest, A[tid])];
-                const int next = tid + 1 < npiece ? L.mrep[tid + 1 + count_below(C, ndest, A[tid + 1])] : rtot.x;
-                L.home[e] = L.cnt[e] - L.piece_n[tid];
-                L.first_rep[e] = first;
-                L.nrep_e[e] = next - first;
-            }
-            merged = true;
         }
-        __syncthreads();
+        if (tid < npiece) {
+            const int e = L.piece_e[tid];
+            const int first = L.mrep[tid + count_below(C, ndest, A[tid])];
+            const int next = tid + 1 < npiece ? L.mrep[tid + 1 + count_below(C, ndest, A[tid + 1])] : rtot.x;
+            L.home[e] = L.cnt[e] - L.piece_n[tid];
+            L.first_rep[e] = first;
+            L.nrep_e[e] = next - first;
+        }
+        merged = !__syncthreads_or(bad || T != tot4.w);
+        if (!merged) {  // undo: the sequential loop starts from the initial results
+            for (int e = tid; e < E; e += kLayoutThreads) {
+                L.home[e] = L.cnt[e];
+                L.first_rep[e] = 0;
+                L.nrep_e[e] = 0;
+            }
+            for (int q = tid; q < R * B; q += kLayoutThreads) L.slot_rep[q] = -1;
+            __syncthreads();
+        }
     }
 
     // Sequential merge (one thread), used when the parallel form does not
