@@ -69,7 +69,7 @@ struct BalanceLds {
     int mrep[kMaxBalanceSlots];      // parallel merge: replicas before each merged breakpoint
     int A[kMaxE];             // start of each piece in the shed stream
     int C[kMaxE];             // start of each destination in the room stream
-    int pre[kMaxE];           // counts in planning order, exclusive prefix
+    int shed[kMaxE];          // entries shed by the expert at each planning position
     int seg_off[kMaxE + kMaxBalanceSlots + 1];
     int2 tmp[kLayoutWaves];
     int4 tmp4[kLayoutWaves];
@@ -107,61 +107,52 @@ __device__ __forceinline__ int4 block_exclusive_scan4(int4 v, int4 *s_tmp, int4 
 __device__ __forceinline__ void plan_balance(BalanceLds &L, int E, int R, int B, int valid) {
     const int tid = threadIdx.x;
     const int epr = E / R, nseg = epr + B, ngrp = R * nseg;
-    // Step 1, from the counts alone: initial results, each rank's room
-    // (quota - load) and each expert's place in its rank's size order (count
-    // descending, id ascending).
+    // Step 1, from the counts alone: initial results, and for every expert its
+    // place in its rank's size order (count descending, id ascending) and the
+    // entries it sheds -- its rank's surplus (load - quota) minus the counts
+    // of the rank's larger experts, clamped to [0, count]: what the sequential
+    // plan takes from it as long as destinations do not run out.  One walk
+    // over the rank's experts gives the place, the larger experts' counts and
+    // the rank's load.  Results go to the expert's planning position (ranks
+    // ascending, size order); the first expert of each rank stores its room.
     for (int e = tid; e < E; e += kLayoutThreads) {
         L.home[e] = L.cnt[e];
         L.first_rep[e] = 0;
         L.nrep_e[e] = 0;
     }
     for (int q = tid; q < R * B; q += kLayoutThreads) L.slot_rep[q] = -1;
-    for (int r = tid; r < R; r += kLayoutThreads) {
-        int load = 0, j = 0;
-        for (; j + 8 <= epr; j += 8) {   // 8 LDS reads in flight
-            int c8[8];
-#pragma unroll
-            for (int u = 0; u < 8; ++u) c8[u] = L.cnt[r * epr + j + u];
-#pragma unroll
-            for (int u = 0; u < 8; ++u) load += c8[u];
-        }
-        for (; j < epr; ++j) load += L.cnt[r * epr + j];
-        L.room[r] = valid / R + (r < valid % R ? 1 : 0) - load;
-    }
     if (tid < E) {
-        const int e = tid, r0 = (e / epr) * epr, c = L.cnt[e];
-        int before = 0, j = r0;
+        const int e = tid, r = e / epr, r0 = r * epr, c = L.cnt[e];
+        int before = 0, larger = 0, load = 0, j = r0;
         for (; j + 8 <= r0 + epr; j += 8) {   // 8 LDS reads in flight
             int c8[8];
 #pragma unroll
             for (int u = 0; u < 8; ++u) c8[u] = L.cnt[j + u];
 #pragma unroll
-            for (int u = 0; u < 8; ++u) before += (c8[u] > c || (c8[u] == c && j + u < e)) ? 1 : 0;
+            for (int u = 0; u < 8; ++u) {
+                const bool ahead = c8[u] > c || (c8[u] == c && j + u < e);
+                before += ahead ? 1 : 0;
+                larger += ahead ? c8[u] : 0;
+                load += c8[u];
+            }
         }
         for (; j < r0 + epr; ++j) {
             const int cj = L.cnt[j];
-            before += (cj > c || (cj == c && j < e)) ? 1 : 0;
+            const bool ahead = cj > c || (cj == c && j < e);
+            before += ahead ? 1 : 0;
+            larger += ahead ? cj : 0;
+            load += cj;
         }
+        const int room = valid / R + (r < valid % R ? 1 : 0) - load;
+        const int my = -room - larger;
         L.order[r0 + before] = e;
+        L.shed[r0 + before] = my < 0 ? 0 : (my > c ? c : my);
+        if (e == r0) L.room[r] = room;
     }
     __syncthreads();
+    const int my = tid < E ? L.shed[tid] : 0;
 
-    // Step 2: entries each expert sheds -- its rank's surplus minus the counts
-    // of the rank's larger experts, clamped to [0, count]: what the sequential
-    // plan takes from it as long as destinations do not run out.  Needs the
-    // counts scanned in planning order (ranks ascending, size order).
-    const int c = tid < E ? L.cnt[L.order[tid]] : 0;
-    int2 tot0;
-    const int2 pre = block_exclusive_scan2(make_int2(c, 0), L.tmp, tot0);
-    if (tid < E) L.pre[tid] = pre.x;
-    __syncthreads();
-    int my = 0;
-    if (tid < E) {
-        const int r = L.order[tid] / epr;
-        my = -L.room[r] - (pre.x - L.pre[r * epr]);
-        my = my < 0 ? 0 : (my > c ? c : my);
-    }
-    // Step 3, one scan for four things: the non-zero pieces compacted in
+    // Step 2, one scan for four things: the non-zero pieces compacted in
     // planning order with their starts in the shed stream (A), and the ranks
     // below their quota (destinations, ascending) with their starts in the
     // room stream (C).
@@ -182,7 +173,7 @@ __device__ __forceinline__ void plan_balance(BalanceLds &L, int E, int R, int B,
     const int npiece = tot4.x, T = tot4.y, ndest = B > 0 ? tot4.z : 0;
     __syncthreads();
 
-    // Step 4: merge of pieces into destinations.  Laid end to end, the pieces
+    // Step 3: merge of pieces into destinations.  Laid end to end, the pieces
     // and the destinations' rooms both cover [0, T): the overloaded ranks'
     // surpluses add up to the other ranks' rooms.  A replica is a non-empty
     // overlap of one piece's span with one destination's span, numbered in
