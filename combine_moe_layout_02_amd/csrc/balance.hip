@@ -292,27 +292,47 @@ __device__ __forceinline__ void plan_balance(BalanceLds &L, int E, int R, int B,
     }
     __syncthreads();
 
-    // segment sizes -> offsets (each thread scans a run of consecutive segments)
-    const int per = (ngrp + kLayoutThreads - 1) / kLayoutThreads;
-    const int g0 = tid * per;
+    // Step 4: segment sizes -> offsets.
     auto seg_size = [&](int g) -> int {
         const int r = g / nseg, j = g % nseg;
         if (j < epr) return L.home[r * epr + j];
         const int q = L.slot_rep[r * B + (j - epr)];
         return q >= 0 ? L.rep_n[q] : 0;
     };
-    int local = 0;
-    for (int g = g0; g < g0 + per && g < ngrp; ++g) local += seg_size(g);
-    int2 total;
-    const int2 ex = block_exclusive_scan2(make_int2(local, 0), L.tmp, total);
-    int run = ex.x;
-    for (int g = g0; g < g0 + per && g < ngrp; ++g) {
-        L.seg_off[g] = run;
-        run += seg_size(g);
+    if (!(L.flags & FLAG_UNBALANCED)) {  // uniform
+        // Every rank holds exactly its quota, so rank r starts after the
+        // quotas of the ranks before it; one wave scans each rank's segments.
+        const int wave = tid / kWave, lane = tid & (kWave - 1);
+        const int c = (nseg + kWave - 1) / kWave;  // segments per lane
+        for (int r = wave; r < R; r += kLayoutWaves) {
+            const int start = r * (valid / R) + min(r, valid % R);
+            const int j0 = min(lane * c, nseg), j1 = min(j0 + c, nseg);
+            int sum = 0;
+            for (int j = j0; j < j1; ++j) sum += seg_size(r * nseg + j);
+            int run = start + wave_inclusive_scan(sum) - sum;
+            for (int j = j0; j < j1; ++j) {
+                const int n = seg_size(r * nseg + j);
+                L.seg_off[r * nseg + j] = run;
+                run += n;
+            }
+        }
+        if (tid == 0) L.seg_off[ngrp] = valid;
+    } else {
+        // each thread scans a run of consecutive segments
+        const int per = (ngrp + kLayoutThreads - 1) / kLayoutThreads;
+        const int g0 = tid * per;
+        int local = 0;
+        for (int g = g0; g < g0 + per && g < ngrp; ++g) local += seg_size(g);
+        int2 total;
+        const int2 ex = block_exclusive_scan2(make_int2(local, 0), L.tmp, total);
+        int run = ex.x;
+        for (int g = g0; g < g0 + per && g < ngrp; ++g) {
+            L.seg_off[g] = run;
+            run += seg_size(g);
+        }
+        if (tid == 0) L.seg_off[ngrp] = total.x;
     }
-    if (tid == 0) L.seg_off[ngrp] = total.x;
     __syncthreads();
-
 }
 
 // Row of the k-th entry (stable t*K+k order) of expert e under the plan:
