@@ -167,6 +167,22 @@ def moe_status_str(status: int) -> str:
     return _lib.moe_status_str(int(status)).decode()
 
 
+class PingPongBuffer:
+    """Two Buffers of one shape used in turn: call i works in buffer i % 2, so
+    the results of call i stay valid while call i + 1 runs -- the double
+    buffer of DeepEP's low-latency kernels (DeepEP analysis, code notes).
+    ``next()`` returns the buffer for the next call; arguments as Buffer."""
+
+    def __init__(self, *args, **kwargs):
+        self.buffers = (Buffer(*args, **kwargs), Buffer(*args, **kwargs))
+        self._i = 0
+
+    def next(self) -> "Buffer":
+        b = self.buffers[self._i]
+        self._i ^= 1
+        return b
+
+
 class CULimitedStream:
     """A HIP stream whose kernels run on at most `num_cus` CUs
     (moe_stream_create_cu_limited), usable as a torch stream."""

@@ -368,6 +368,32 @@ def test_bench_step(moe, name):
                            f"bench {name} combine")
 
 
+def test_ping_pong_buffer(moe):
+    """Two decode calls back to back through PingPongBuffer: the first call's
+    results are still exact after the second call ran."""
+    cfg = CONFIGS["decode"]
+    say("case ping-pong decode")
+    pp = moe.PingPongBuffer(cfg.S, cfg.H, cfg.K, cfg.E, cfg.R, fp8=True, pad_mode=cfg.pad_mode,
+                            pad_rows=cfg.pad_rows, device=DEV)
+    calls = []
+    for seed in (31, 32):
+        w = make_workload(cfg, seed=seed)
+        buf = pp.next()
+        buf.dispatch(dev_bf16(w.hidden, DEV), torch.from_numpy(w.topk_w).to(DEV),
+                     torch.from_numpy(w.topk_idx).to(DEV))
+        calls.append((w, buf))
+    assert calls[0][1] is not calls[1][1] and pp.next() is calls[0][1]
+    torch.cuda.synchronize()
+    for w, buf in calls:
+        ref = oracle.layout(w.topk_idx, cfg.E, cfg.R, cfg.pad_mode, cfg.pad_rows)
+        compare_layout(buf.layout, ref, "ping-pong layout")
+        valid = ref.src >= 0
+        rc, rs, rw = oracle.dispatch_fp8(w.hidden, ref.pos, len(ref.src), w.topk_w)
+        assert np.array_equal(buf.recv.cpu().numpy()[valid], rc[valid])
+        assert np.array_equal(buf.recv_scales.cpu().numpy()[valid].view(np.uint32), rs[valid].view(np.uint32))
+        assert np.array_equal(buf.recv_w.cpu().numpy()[valid].view(np.uint32), rw[valid].view(np.uint32))
+
+
 @pytest.mark.parametrize("form", ["three-calls", "fused"])
 def test_graph_replay(moe, form):
     """Layout + dispatch + combine captured once in a HIP graph and replayed on
