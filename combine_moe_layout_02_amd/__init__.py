@@ -24,7 +24,7 @@ MOE_FLAG_BAD_EXPERT, MOE_FLAG_CAPACITY, MOE_FLAG_UNBALANCED = 1, 2, 4
 
 EXPORTED = ("moe_max_recv_rows", "moe_layout_workspace_bytes", "moe_layout", "moe_dispatch",
             "moe_layout_dispatch", "moe_combine", "moe_layout_balanced_workspace_bytes", "moe_layout_balanced",
-            "moe_stream_create_cu_limited", "moe_stream_destroy", "moe_status_str")
+            "moe_zero_padding", "moe_stream_create_cu_limited", "moe_stream_destroy", "moe_status_str")
 
 
 class MoeError(RuntimeError):
@@ -68,6 +68,8 @@ def _load():
     L.moe_layout_dispatch.restype = ctypes.c_int
     L.moe_combine.argtypes = [D, B, P, ctypes.c_int32, P, P, P, P]
     L.moe_combine.restype = ctypes.c_int
+    L.moe_zero_padding.argtypes = [D, B, ctypes.c_int32, ctypes.c_int32, P, P, P]
+    L.moe_zero_padding.restype = ctypes.c_int
     L.moe_layout_balanced_workspace_bytes.argtypes = [D, ctypes.c_int32]
     L.moe_layout_balanced_workspace_bytes.restype = ctypes.c_size_t
     L.moe_layout_balanced.argtypes = [D, ctypes.c_int32, P, B, ctypes.POINTER(moe_balance_bufs), P,
@@ -373,6 +375,23 @@ def moe_combine(desc: LayoutDesc, layout: Layout, expert_out: torch.Tensor, w=No
     return out
 
 
+def moe_zero_padding(desc: LayoutDesc, layout: Layout, recv: torch.Tensor, recv_scales=None, stream=None):
+    """Zero every receive row that no entry maps to (and its FP8 scales).
+    FP8 when recv holds bytes (uint8), bf16 otherwise."""
+    fp8 = recv.dtype == torch.uint8
+    H = recv.shape[-1]
+    _check(recv, "recv", torch.uint8 if fp8 else torch.bfloat16)
+    if recv.shape[0] < moe_max_recv_rows(desc):
+        raise ValueError("recv must hold moe_max_recv_rows rows")
+    if fp8:
+        _check(recv_scales, "recv_scales", torch.float32, (recv.shape[0], H // 128))
+    d, b = desc.c(), layout.c()
+    rc = _lib.moe_zero_padding(ctypes.byref(d), ctypes.byref(b), H, 1 if fp8 else 0, _ptr(recv),
+                               _ptr(recv_scales) if fp8 else None, _stream(stream, recv.device))
+    if rc != MOE_OK:
+        raise MoeError(rc, "moe_zero_padding")
+
+
 # ---------------------------------------------------------------------------
 # Static-shape buffer: validate once, then bare C calls
 # ---------------------------------------------------------------------------
@@ -484,6 +503,13 @@ class Buffer:
                               self._out, _stream(stream, self.device))
         if rc != MOE_OK:
             raise MoeError(rc, "moe_combine")
+
+    def zero_padding_call(self, stream=None):
+        """moe_zero_padding on this buffer's receive rows (after a dispatch)."""
+        rc = _lib.moe_zero_padding(self._dp, self._bp, self.H, 1 if self.fp8 else 0, self._recv, self._scales,
+                                   _stream(stream, self.device))
+        if rc != MOE_OK:
+            raise MoeError(rc, "moe_zero_padding")
 
     def dispatch(self, hidden, topk_w, topk_idx, stream=None):
         """Layout + dispatch.  Returns (recv, recv_w, expert_offset, recv_scales)."""

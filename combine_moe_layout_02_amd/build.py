@@ -19,7 +19,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libmoe_ep.so")
-SOURCES = ["api.hip", "layout.hip", "dispatch.hip", "combine.hip", "fused.hip", "balance.hip"]
+SOURCES = ["api.hip", "layout.hip", "dispatch.hip", "combine.hip", "fused.hip", "balance.hip", "padding.hip"]
 ARCH = "gfx950"
 
 COMMON_FLAGS = [

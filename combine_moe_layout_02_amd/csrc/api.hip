@@ -9,6 +9,11 @@
 #include "moe_ep.h"
 #include "moe_kernels.h"
 
+namespace moe {
+hipError_t launch_zero_padding(const int32_t *src, int rows, int row_bytes, void *recv, float *scales, int nsc,
+                               hipStream_t s);  // padding.hip
+}
+
 namespace {
 
 bool desc_ok(const moe_layout_desc *d) {
@@ -199,6 +204,22 @@ moe_status moe_combine(const moe_layout_desc *desc, const moe_layout_bufs *layou
 size_t moe_layout_balanced_workspace_bytes(const moe_layout_desc *desc, int32_t slots_per_rank) {
     if (desc == nullptr || !desc_ok(desc) || slots_per_rank < 0) return 0;
     return moe::balance_workspace_bytes(static_cast<int64_t>(desc->S) * desc->K, desc->E, desc->R);
+}
+
+moe_status moe_zero_padding(const moe_layout_desc *desc, const moe_layout_bufs *layout, int32_t H, int32_t fp8,
+                            void *recv, float *recv_scales, void *stream) {
+    if (desc == nullptr || layout == nullptr) return MOE_ERR_NULL;
+    if (!desc_ok(desc) || max_rows(desc) < 0 || H < 8 || H % 8 != 0 || (fp8 && H % 128 != 0)) return MOE_ERR_SHAPE;
+    const int64_t rows = max_rows(desc);
+    if (rows == 0) return MOE_OK;
+    if (layout->src == nullptr || recv == nullptr || (fp8 && recv_scales == nullptr)) return MOE_ERR_NULL;
+    if (!aligned(layout->src, 4) || !aligned(recv, 16) || !aligned(recv_scales, 4)) return MOE_ERR_ALIGN;
+    const int row_bytes = fp8 ? H : 2 * H;
+    return moe::launch_zero_padding(layout->src, static_cast<int>(rows), row_bytes, recv,
+                                    fp8 ? recv_scales : nullptr, H / 128, static_cast<hipStream_t>(stream)) ==
+                   hipSuccess
+               ? MOE_OK
+               : MOE_ERR_HIP;
 }
 
 moe_status moe_layout_balanced(const moe_layout_desc *desc, int32_t slots_per_rank, const int32_t *topk_idx,

@@ -174,6 +174,21 @@ moe_status moe_combine(const moe_layout_desc *desc, const moe_layout_bufs *layou
                        const void *expert_out, int32_t H, const float *w,
                        const void *shared_out, void *out, void *stream);
 
+/* Zero padding (optional, after dispatch): clears every receive row that no
+ * entry maps to -- src[r] = -1: padding inside the segments and the unused
+ * tail -- so a consumer that runs over whole padded segments reads zeros
+ * there (search-results page, the snippet on the limits of dynamic routing:
+ * drop tokens or zero-pad).  Dispatch itself never writes those rows.
+ *   layout      moe_layout's output for this batch (its src is read).
+ *   H, fp8      as given to moe_dispatch.
+ *   recv        [max_recv,H] bf16 or E4M3 bytes, 16-byte aligned.
+ *   recv_scales [max_recv,H/128] fp32 (required when fp8, ignored otherwise);
+ *               scale rows of cleared rows become 0.0f.
+ * Rows that hold an entry are not written.  Cost: one write of every padding
+ * row (at the decode shape 31,744 rows x 7 KB). */
+moe_status moe_zero_padding(const moe_layout_desc *desc, const moe_layout_bufs *layout, int32_t H, int32_t fp8,
+                            void *recv, float *recv_scales, void *stream);
+
 /* Balanced layout: every rank receives the same number of rows (N/R, the
  * first N%R ranks one more; N = entries with a valid expert) however skewed
  * the routing, through redundant copies of experts held in per-rank slots --

@@ -74,6 +74,8 @@ def lib():
         L.oracle_e4m3_from_f32_n.argtypes = [P, i64, P]
         L.oracle_e4m3_from_f32_n.restype = None
         L.oracle_dequant_identity.argtypes = [P, P, i64, i32, P]
+        L.oracle_zero_padding.argtypes = [P, i64, i64, P, P, i32]
+        L.oracle_zero_padding.restype = None
         L.oracle_dequant_identity.restype = None
         _lib = L
     return _lib
@@ -254,6 +256,18 @@ def combine(expert_out: np.ndarray, pos: np.ndarray, w: Optional[np.ndarray] = N
     if rc != OK:
         raise ValueError(f"oracle_combine failed with {rc}")
     return out
+
+
+def zero_padding(src: np.ndarray, recv: np.ndarray, recv_scales=None):
+    """Copies of recv (and recv_scales) with every row whose src is -1 zeroed."""
+    srcs = _c(src, np.int32)
+    out = np.array(recv, copy=True, order="C")
+    rows = out.shape[0]
+    row_bytes = out.reshape(rows, -1).view(np.uint8).shape[1]
+    sc = None if recv_scales is None else np.array(recv_scales, dtype=np.float32, copy=True, order="C")
+    lib().oracle_zero_padding(_p(srcs), rows, row_bytes, _p(out), None if sc is None else _p(sc),
+                              0 if sc is None else sc.shape[1])
+    return out, sc
 
 
 def dequant_identity_expert(recv_codes: np.ndarray, recv_scales: np.ndarray) -> np.ndarray:

@@ -334,6 +334,23 @@ void oracle_dequant_identity(const uint8_t *codes, const float *scales, int64_t 
         }
 }
 
+/* Zero padding (optional, after dispatch): static per-expert segments are
+ * filled up with zeros (search-results page, the snippet on dynamic-routing
+ * limits: tokens are dropped or segments zero-padded).  Every receive row that
+ * no entry maps to (src[r] = -1: padding inside a segment and the unused tail)
+ * becomes all-zero bytes, and with FP8 its scale row becomes 0.0f; rows that
+ * hold an entry are left as they are.  recv [rows, row_bytes] bytes,
+ * scales [rows, nsc] or NULL. */
+void oracle_zero_padding(const int32_t *src, int64_t rows, int64_t row_bytes, uint8_t *recv, float *scales,
+                         int nsc) {
+    for (int64_t r = 0; r < rows; ++r) {
+        if (src[r] >= 0) continue;
+        for (int64_t b = 0; b < row_bytes; ++b) recv[r * row_bytes + b] = 0;
+        if (scales != NULL)
+            for (int j = 0; j < nsc; ++j) scales[r * nsc + j] = 0.0f;
+    }
+}
+
 /* ------------------------------------------------------------------------ */
 /* Balanced layout (redundant expert slots)                                   */
 /* ------------------------------------------------------------------------ */

@@ -120,6 +120,25 @@ def test_dispatch_combine_argument_errors(moe):
     assert lib.moe_combine(ctypes.byref(e), ctypes.byref(b), None, 256, None, None, None, None) == moe.MOE_OK
 
 
+def test_zero_padding_argument_errors(moe):
+    """moe_zero_padding rejects bad arguments before any launch."""
+    lib = moe.lib()
+    P = ctypes.c_void_p
+    d = moe.LayoutDesc(64, 2, 8, 2, moe.MOE_PAD_CAPACITY, 20).c()
+    b = _bufs(moe)
+    assert lib.moe_zero_padding(None, ctypes.byref(b), 256, 0, P(FAKE), None, None) == moe.MOE_ERR_NULL
+    assert lib.moe_zero_padding(ctypes.byref(d), None, 256, 0, P(FAKE), None, None) == moe.MOE_ERR_NULL
+    assert lib.moe_zero_padding(ctypes.byref(d), ctypes.byref(b), 12, 0, P(FAKE), None, None) == moe.MOE_ERR_SHAPE
+    assert lib.moe_zero_padding(ctypes.byref(d), ctypes.byref(b), 264, 1, P(FAKE), P(FAKE), None) == \
+        moe.MOE_ERR_SHAPE                                            # FP8 needs H % 128 == 0
+    assert lib.moe_zero_padding(ctypes.byref(d), ctypes.byref(b), 256, 1, P(FAKE), None, None) == moe.MOE_ERR_NULL
+    assert lib.moe_zero_padding(ctypes.byref(d), ctypes.byref(b), 256, 0, None, None, None) == moe.MOE_ERR_NULL
+    assert lib.moe_zero_padding(ctypes.byref(d), ctypes.byref(b), 256, 0, P(FAKE + 8), None, None) == \
+        moe.MOE_ERR_ALIGN
+    e = moe.LayoutDesc(0, 2, 8, 2).c()                               # empty batch: nothing to do
+    assert lib.moe_zero_padding(ctypes.byref(e), ctypes.byref(b), 256, 0, None, None, None) == moe.MOE_OK
+
+
 def test_balanced_workspace_rule(moe):
     """The balanced layout needs no scratch up to 32K entries (one launch) and
     reports MOE_ERR_WORKSPACE above that when none is given.  No launch."""

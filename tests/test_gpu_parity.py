@@ -368,6 +368,49 @@ def test_bench_step(moe, name):
                            f"bench {name} combine")
 
 
+@pytest.mark.parametrize("name", ["decode", "skew"])
+def test_zero_padding(moe, name):
+    """moe_zero_padding after dispatch: the whole receive buffer (and FP8
+    scales), padding rows included, equals the oracle's dispatch followed by its
+    zero padding, bit for bit."""
+    cfg = CONFIGS[name]
+    w = make_workload(cfg)
+    say(f"case zero-padding {name}")
+    desc = moe.LayoutDesc(cfg.S, cfg.K, cfg.E, cfg.R, cfg.pad_mode, cfg.pad_rows)
+    rows = moe.moe_max_recv_rows(desc)
+    idx = torch.from_numpy(w.topk_idx).to(DEV)
+    lay = moe.moe_layout(desc, idx)
+    ref = oracle.layout(w.topk_idx, cfg.E, cfg.R, cfg.pad_mode, cfg.pad_rows)
+    pad = ref.src < 0
+    assert pad.any()
+    if cfg.fp8:
+        recv = torch.full((rows, cfg.H), POISON_U8, dtype=torch.uint8, device=DEV)
+        scales = torch.full((rows, cfg.H // 128), float("nan"), dtype=torch.float32, device=DEV)
+        moe.moe_dispatch(desc, lay, dev_bf16(w.hidden, DEV), idx, fp8=True, recv=recv, recv_scales=scales)
+        moe.moe_zero_padding(desc, lay, recv, scales)
+        torch.cuda.synchronize()
+        rc, rs, _ = oracle.dispatch_fp8(w.hidden, ref.pos, rows)
+        want_c, want_s = oracle.zero_padding(ref.src, rc, rs)
+        assert np.array_equal(recv.cpu().numpy(), want_c)
+        assert np.array_equal(scales.cpu().numpy().view(np.uint32), want_s.view(np.uint32))
+        # the same through Buffer's prepared call
+        buf = moe.Buffer(cfg.S, cfg.H, cfg.K, cfg.E, cfg.R, fp8=True, pad_mode=cfg.pad_mode,
+                         pad_rows=cfg.pad_rows, device=DEV)
+        buf.recv.fill_(POISON_U8)
+        buf.dispatch(dev_bf16(w.hidden, DEV), torch.from_numpy(w.topk_w).to(DEV), idx)
+        buf.zero_padding_call()
+        torch.cuda.synchronize()
+        assert np.array_equal(buf.recv.cpu().numpy(), want_c)
+    else:
+        recv = torch.full((rows, cfg.H), POISON_BF16, dtype=torch.int16, device=DEV).view(torch.bfloat16)
+        moe.moe_dispatch(desc, lay, dev_bf16(w.hidden, DEV), idx, fp8=False, recv=recv)
+        moe.moe_zero_padding(desc, lay, recv)
+        torch.cuda.synchronize()
+        rb, _ = oracle.dispatch_bf16(w.hidden, ref.pos, rows)
+        want, _ = oracle.zero_padding(ref.src, rb)
+        assert np.array_equal(host_bits(recv), want)
+
+
 def test_ping_pong_buffer(moe):
     """Two decode calls back to back through PingPongBuffer: the first call's
     results are still exact after the second call ran."""

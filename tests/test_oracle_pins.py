@@ -651,3 +651,34 @@ def test_balanced_skew_config():
     lo8 = oracle.layout_balanced(w.topk_idx, cfg.E, cfg.R, 8)
     assert int(lo8.status[0]) == oracle.FLAG_UNBALANCED
     check_balanced(lo8, w.topk_idx, cfg.E, cfg.R, 8)
+
+
+def test_zero_padding_hand_example():
+    src = np.array([0, -1, 2, -1], np.int32)
+    rng = np.random.default_rng(3)
+    recv = rng.integers(1, 255, (4, 16)).astype(np.uint8)
+    scales = rng.random((4, 2)).astype(np.float32) + 1.0
+    out, sc = oracle.zero_padding(src, recv, scales)
+    assert np.array_equal(out[[0, 2]], recv[[0, 2]]) and np.array_equal(sc[[0, 2]], scales[[0, 2]])
+    assert not out[[1, 3]].any() and not sc[[1, 3]].any()
+    out16, none = oracle.zero_padding(src, recv.view(np.uint16))     # bf16 rows, no scales
+    assert none is None and np.array_equal(out16.view(np.uint8)[[0, 2]], recv[[0, 2]])
+    assert not out16[[1, 3]].any()
+
+
+def test_zero_padding_after_padded_dispatch():
+    """On a capacity-padded layout, after zero padding every receive row either
+    holds the codes of the token its src names or is all zero (codes and scale)."""
+    cfg = CONFIGS["decode"]
+    w = make_workload(cfg)
+    lo = oracle.layout(w.topk_idx, cfg.E, cfg.R, cfg.pad_mode, cfg.pad_rows)
+    rows = len(lo.src)
+    codes, scales, _ = oracle.dispatch_fp8(w.hidden, lo.pos, rows)
+    codes[lo.src < 0] = 0xA5                         # stale bytes where nothing was written
+    scales[lo.src < 0] = 7.0
+    zc, zs = oracle.zero_padding(lo.src, codes, scales)
+    pad = lo.src < 0
+    assert pad.sum() == rows - cfg.S * cfg.K
+    assert not zc[pad].any() and not zs[pad].any()
+    q = np.stack([oracle.quantize_row_fp8(w.hidden[t])[0] for t in range(cfg.S)])
+    assert np.array_equal(zc[~pad], q[lo.src[~pad] // cfg.K])
