@@ -14,6 +14,14 @@
  *                 of each token's K rows (fp32 accumulation), plus an optional
  *                 shared-expert output.
  *
+ * Around them: moe_layout_dispatch (layout + dispatch in one launch for
+ * decode-sized batches), moe_layout_balanced (every rank receives the same
+ * number of rows through redundant-expert slots), moe_zero_padding (optional
+ * zero fill of padding rows), moe_stream_create_cu_limited /
+ * moe_stream_destroy (a stream confined to N CUs), and the sizing helpers
+ * moe_max_recv_rows, moe_layout_workspace_bytes,
+ * moe_layout_balanced_workspace_bytes, plus moe_status_str.
+ *
  * What the operations are (passages):
  *   - Experts of a layer are spread over the ranks of an EP group; E must
  *     divide by the group size R and each rank holds E/R local experts
