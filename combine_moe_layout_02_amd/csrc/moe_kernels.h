@@ -151,8 +151,8 @@ __device__ __forceinline__ uint64_t match_key(int key, bool active, int nbits) {
 // 1, 2, 4 and 8 lanes inside each row of 16 (lanes shifted in from outside the
 // row add 0), then lane 15's sum is added to row 1 and lane 47's to row 3,
 // then lane 31's to rows 2 and 3.  On MI355X about 100 cycles against ~480 for
-// the same scan through six cross-lane shuffles.  All 64 lanes must be active
-// (a lane outside EXEC would contribute whatever its register holds).
+// the same scan through six cross-lane shuffles.  All 64 lanes must be active:
+// the cross-lane reads do not skip inactive lanes.
 __device__ __forceinline__ int wave_inclusive_scan(int v) {
     v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, false);  // row_shr:1
     v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, false);  // row_shr:2
