@@ -377,10 +377,10 @@ def moe_combine(desc: LayoutDesc, layout: Layout, expert_out: torch.Tensor, w=No
 
 def moe_zero_padding(desc: LayoutDesc, layout: Layout, recv: torch.Tensor, recv_scales=None, stream=None):
     """Zero every receive row that no entry maps to (and its FP8 scales).
-    FP8 when recv holds bytes (uint8), bf16 otherwise."""
-    fp8 = recv.dtype == torch.uint8
+    FP8 when recv holds E4M3 codes (uint8 or float8_e4m3fn), bf16 otherwise."""
+    fp8 = recv.dtype in (torch.uint8, torch.float8_e4m3fn)
     H = recv.shape[-1]
-    _check(recv, "recv", torch.uint8 if fp8 else torch.bfloat16)
+    _check(recv, "recv", (torch.uint8, torch.float8_e4m3fn) if fp8 else torch.bfloat16)
     if recv.shape[0] < moe_max_recv_rows(desc):
         raise ValueError("recv must hold moe_max_recv_rows rows")
     if fp8:
