@@ -349,6 +349,56 @@ def cu_budget_numbers(moe, run, counts, steps: int = 10):
     return out
 
 
+def overlap_numbers(moe, run, dev, steps: int = 10, gemms: int = 4):
+    """The step on one half of the CUs while a bf16 GEMM of the layer's shape
+    ([S,H] x [H,H]) runs on the other half: each alone, then both at once."""
+    import torch
+    n_cu = torch.cuda.get_device_properties(dev).multi_processor_count
+    half = n_cu // 2
+    cfg = run.cfg
+    a = torch.randn(cfg.S, cfg.H, device=dev, dtype=torch.float32).to(torch.bfloat16)
+    b = torch.randn(cfg.H, cfg.H, device=dev, dtype=torch.float32).to(torch.bfloat16)
+    c = torch.empty(cfg.S, cfg.H, device=dev, dtype=torch.bfloat16)
+    _, db, cb = run.bytes()
+    with moe.CULimitedStream(half, dev, first_cu=0) as sa, moe.CULimitedStream(half, dev, first_cu=half) as sb:
+        def on_a():
+            for _ in range(steps):
+                run.step()
+
+        def on_b():
+            for _ in range(gemms):
+                torch.matmul(a, b, out=c)
+
+        def timed(work):   # list of (stream, fn): ms per stream, and the whole span
+            torch.cuda.synchronize()
+            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in work]
+            t0 = time.perf_counter()
+            for (st, fn), (e0, e1) in zip(work, ev):
+                with torch.cuda.stream(st):
+                    e0.record()
+                    fn()
+                    e1.record()
+            torch.cuda.synchronize()
+            wall = (time.perf_counter() - t0) * 1e3
+            return [e0.elapsed_time(e1) for e0, e1 in ev], wall
+
+        for st, fn in ((sa.stream, on_a), (sb.stream, on_b)):   # warm-up
+            with torch.cuda.stream(st):
+                fn()
+        (t_a,), _ = timed([(sa.stream, on_a)])
+        (t_b,), _ = timed([(sb.stream, on_b)])
+        (ta2, tb2), wall = timed([(sa.stream, on_a), (sb.stream, on_b)])
+    del a, b, c
+    flops = 2.0 * cfg.S * cfg.H * cfg.H * gemms
+    return {"cus_each": half, "steps": steps, "gemm": f"{gemms} x bf16 [{cfg.S}x{cfg.H}] x [{cfg.H}x{cfg.H}]",
+            "step_alone_us": round(t_a / steps * 1e3, 1), "gemm_alone_us": round(t_b / gemms * 1e3, 1),
+            "step_overlapped_us": round(ta2 / steps * 1e3, 1), "gemm_overlapped_us": round(tb2 / gemms * 1e3, 1),
+            "dispatch_plus_combine_gbps_overlapped": round((db + cb) * steps / (ta2 * 1e-3) / 1e9, 1),
+            "gemm_tflops_alone": round(flops / (t_b * 1e-3) / 1e12, 1),
+            "gemm_tflops_overlapped": round(flops / (tb2 * 1e-3) / 1e12, 1),
+            "sum_alone_over_both_wall": round((t_a + t_b) / wall, 3)}
+
+
 def balanced_numbers(moe, cfg, dev, slots: int = 16, iters: int = 200):
     """Balanced layout (redundant-expert slots) on a skewed batch: time per
     call next to the plain layout, and rows per rank before / after."""
@@ -516,6 +566,7 @@ def main(argv=None):
     balanced = None if args.no_decode else balanced_numbers(moe, CONFIGS["skew"], dev)
     budgets = [int(x) for x in args.cu_budgets.split(",") if x.strip()]
     cu_budget = cu_budget_numbers(moe, run, budgets) if budgets else None
+    overlap = overlap_numbers(moe, run, dev) if budgets else None
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -529,7 +580,7 @@ def main(argv=None):
                    "fp8_dispatch": cfg.fp8, "routing": cfg.routing, "pad_mode": cfg.pad_mode,
                    "pad_rows": cfg.pad_rows, "shared": cfg.shared, "parallelism": f"ep{cfg.R} simulated on 1 GPU"},
         "roofline": roofline, "cpu_baseline": cpu, "kernels": extra, "decode": decode,
-        "cu_budget": cu_budget, "balanced_layout": balanced, "percentiles": pct, "same_shape_skew": also,
+        "cu_budget": cu_budget, "overlap": overlap, "balanced_layout": balanced, "percentiles": pct, "same_shape_skew": also,
     }
     print(json.dumps(line), flush=True)
 

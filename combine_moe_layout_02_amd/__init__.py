@@ -24,7 +24,8 @@ MOE_FLAG_BAD_EXPERT, MOE_FLAG_CAPACITY, MOE_FLAG_UNBALANCED = 1, 2, 4
 
 EXPORTED = ("moe_max_recv_rows", "moe_layout_workspace_bytes", "moe_layout", "moe_dispatch",
             "moe_layout_dispatch", "moe_combine", "moe_layout_balanced_workspace_bytes", "moe_layout_balanced",
-            "moe_zero_padding", "moe_stream_create_cu_limited", "moe_stream_destroy", "moe_status_str")
+            "moe_zero_padding", "moe_stream_create_cu_limited", "moe_stream_create_cu_range", "moe_stream_destroy",
+            "moe_status_str")
 
 
 class MoeError(RuntimeError):
@@ -77,6 +78,8 @@ def _load():
     L.moe_layout_balanced.restype = ctypes.c_int
     L.moe_stream_create_cu_limited.argtypes = [ctypes.c_int32, ctypes.POINTER(ctypes.c_void_p)]
     L.moe_stream_create_cu_limited.restype = ctypes.c_int
+    L.moe_stream_create_cu_range.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.POINTER(ctypes.c_void_p)]
+    L.moe_stream_create_cu_range.restype = ctypes.c_int
     L.moe_stream_destroy.argtypes = [P]
     L.moe_stream_destroy.restype = ctypes.c_int
     L.moe_status_str.argtypes = [ctypes.c_int32]
@@ -186,14 +189,15 @@ class PingPongBuffer:
 
 
 class CULimitedStream:
-    """A HIP stream whose kernels run on at most `num_cus` CUs
-    (moe_stream_create_cu_limited), usable as a torch stream."""
+    """A HIP stream whose kernels run only on CUs [first_cu, first_cu +
+    num_cus) (moe_stream_create_cu_range; first_cu = 0 is
+    moe_stream_create_cu_limited), usable as a torch stream."""
 
-    def __init__(self, num_cus: int, device="cuda"):
+    def __init__(self, num_cus: int, device="cuda", first_cu: int = 0):
         handle = ctypes.c_void_p()
-        rc = _lib.moe_stream_create_cu_limited(int(num_cus), ctypes.byref(handle))
+        rc = _lib.moe_stream_create_cu_range(int(first_cu), int(num_cus), ctypes.byref(handle))
         if rc != MOE_OK:
-            raise MoeError(rc, "moe_stream_create_cu_limited")
+            raise MoeError(rc, "moe_stream_create_cu_range")
         self.num_cus = num_cus
         self.handle = handle.value
         self.stream = torch.cuda.ExternalStream(self.handle, device=torch.device(device))

@@ -257,19 +257,21 @@ moe_status moe_layout_balanced(const moe_layout_desc *desc, int32_t slots_per_ra
                ? MOE_OK : MOE_ERR_HIP;
 }
 
-moe_status moe_stream_create_cu_limited(int32_t num_cus, void **stream_out) {
+moe_status moe_stream_create_cu_range(int32_t first_cu, int32_t num_cus, void **stream_out) {
     if (stream_out == nullptr) return MOE_ERR_NULL;
     int dev = 0, xcc = 1;
     hipDeviceProp_t prop;
     if (hipGetDevice(&dev) != hipSuccess || hipGetDeviceProperties(&prop, dev) != hipSuccess) return MOE_ERR_HIP;
     if (hipDeviceGetAttribute(&xcc, hipDeviceAttributeNumberOfXccs, dev) != hipSuccess || xcc < 1) xcc = 1;
     const int total = prop.multiProcessorCount;
-    // Bit i of the queue CU mask selects a CU of XCD i % xcc, so the first
-    // num_cus bits give every XCD num_cus / xcc CUs; a mask that leaves an XCD
+    // Bit i of the queue CU mask selects a CU of XCD i % xcc, so a run of bits
+    // starting at a multiple of xcc with a length that is a multiple of xcc
+    // gives every XCD the same number of CUs; a mask that leaves an XCD
     // without CUs is refused by the runtime.
-    if (num_cus < 1 || num_cus > total || num_cus % xcc != 0) return MOE_ERR_SHAPE;
+    if (first_cu < 0 || num_cus < 1 || first_cu % xcc != 0 || num_cus % xcc != 0 || first_cu + num_cus > total)
+        return MOE_ERR_SHAPE;
     std::vector<uint32_t> mask((total + 31) / 32, 0u);
-    for (int i = 0; i < num_cus; ++i) mask[i / 32] |= 1u << (i % 32);
+    for (int i = first_cu; i < first_cu + num_cus; ++i) mask[i / 32] |= 1u << (i % 32);
     hipStream_t s = nullptr;
     if (hipExtStreamCreateWithCUMask(&s, static_cast<uint32_t>(mask.size()), mask.data()) != hipSuccess) {
         (void)hipGetLastError();
@@ -277,6 +279,10 @@ moe_status moe_stream_create_cu_limited(int32_t num_cus, void **stream_out) {
     }
     *stream_out = s;
     return MOE_OK;
+}
+
+moe_status moe_stream_create_cu_limited(int32_t num_cus, void **stream_out) {
+    return moe_stream_create_cu_range(0, num_cus, stream_out);
 }
 
 moe_status moe_stream_destroy(void *stream) {

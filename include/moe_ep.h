@@ -18,7 +18,8 @@
  * decode-sized batches), moe_layout_balanced (every rank receives the same
  * number of rows through redundant-expert slots), moe_zero_padding (optional
  * zero fill of padding rows), moe_stream_create_cu_limited /
- * moe_stream_destroy (a stream confined to N CUs), and the sizing helpers
+ * moe_stream_create_cu_range / moe_stream_destroy (a stream confined to a set
+ * of CUs), and the sizing helpers
  * moe_max_recv_rows, moe_layout_workspace_bytes,
  * moe_layout_balanced_workspace_bytes, plus moe_status_str.
  *
@@ -244,6 +245,14 @@ moe_status moe_layout_balanced(const moe_layout_desc *desc, int32_t slots_per_ra
  * MOE_ERR_SHAPE if num_cus is outside [1, CU count] or not a multiple of the
  * XCD count (8 on MI355X). */
 moe_status moe_stream_create_cu_limited(int32_t num_cus, void **stream_out);
+
+/* The same with the CU set placed: CUs [first_cu, first_cu + num_cus) in the
+ * queue-mask numbering (CU i is on XCD i % XCD count), so two streams with
+ * disjoint ranges split the chip -- e.g. layout / dispatch / combine on one
+ * half and expert compute on the other.  first_cu and num_cus must be
+ * multiples of the XCD count, the range within the CU count; else
+ * MOE_ERR_SHAPE.  moe_stream_create_cu_limited(n) is the range [0, n). */
+moe_status moe_stream_create_cu_range(int32_t first_cu, int32_t num_cus, void **stream_out);
 moe_status moe_stream_destroy(void *stream);
 
 /* Static string naming a moe_status value. */

@@ -156,6 +156,11 @@ def test_balanced_workspace_rule(moe):
     assert lib.moe_layout_balanced(*args, P(FAKE + 16), need, None) == moe.MOE_ERR_ALIGN
 
 
+def test_cu_range_stream_null_output(moe):
+    assert moe.lib().moe_stream_create_cu_range(0, 8, None) == moe.MOE_ERR_NULL
+    assert moe.lib().moe_stream_create_cu_limited(8, None) == moe.MOE_ERR_NULL
+
+
 def test_status_strings(moe):
     for s in range(6):
         assert moe.moe_status_str(s).startswith("MOE_")

@@ -9,6 +9,8 @@ must stay untouched by dispatch and unread by combine.
 """
 from __future__ import annotations
 
+import ctypes
+
 import numpy as np
 import pytest
 import torch
@@ -687,12 +689,20 @@ def test_cu_limited_stream(moe):
 
     want = run()
     torch.cuda.synchronize()
-    with moe.CULimitedStream(32, DEV) as cs:
-        with torch.cuda.stream(cs.stream):
-            got = run()
-        torch.cuda.synchronize()
-    for a, b in zip(got, want):
-        assert torch.equal(a, b)
+    n_cu = torch.cuda.get_device_properties(0).multi_processor_count
+    # the first 32 CUs, and the upper half of the chip (a placed range)
+    for first, count in ((0, 32), (n_cu // 2, n_cu // 2)):
+        with moe.CULimitedStream(count, DEV, first_cu=first) as cs:
+            with torch.cuda.stream(cs.stream):
+                got = run()
+            torch.cuda.synchronize()
+        for a, b in zip(got, want):
+            assert torch.equal(a, b)
+    # ranges the XCD rule refuses
+    handle = ctypes.c_void_p()
+    lib = moe.lib()
+    assert lib.moe_stream_create_cu_range(4, 32, ctypes.byref(handle)) == moe.MOE_ERR_SHAPE
+    assert lib.moe_stream_create_cu_range(n_cu - 8, 16, ctypes.byref(handle)) == moe.MOE_ERR_SHAPE
 
 
 BAL = [
