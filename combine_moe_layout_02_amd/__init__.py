@@ -130,13 +130,23 @@ class Layout:
 
 
 def _ptr(t: Optional[torch.Tensor]):
-    return None if t is None else ctypes.c_void_p(t.data_ptr())
+    return None if t is None else t.data_ptr()   # argtypes make it a void*
 
 
-def _stream(stream, device) -> ctypes.c_void_p:
-    if stream is None:
-        stream = torch.cuda.current_stream(device)
-    return ctypes.c_void_p(stream.cuda_stream)
+# torch's raw current-stream query: measured ~0.1 us per call against ~2 us
+# for torch.cuda.current_stream(), which builds a Stream object.  A
+# decode-sized call costs only a few microseconds on the GPU, so the host side
+# of every call counts.
+_raw_current_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+
+
+def _stream(stream, device) -> int:
+    """Raw hipStream_t of `stream`, or of the current stream of `device`."""
+    if stream is not None:
+        return stream.cuda_stream
+    if _raw_current_stream is not None:
+        return _raw_current_stream(device.index)
+    return torch.cuda.current_stream(device).cuda_stream
 
 
 def _check(t: Optional[torch.Tensor], name: str, dtype, shape=None, device=None):

@@ -6,296 +6,302 @@
 // call's layout and dispatch run in one launch instead of two: the results are
 // exactly those of moe_layout followed by moe_dispatch.
 //
-// Every workgroup owns one token and a slice of its row.  It first issues the
-// loads of its row slice (they do not depend on the layout), then rebuilds in
-// LDS only what its token needs: per-expert counts of all S*K entries and of
-// the entries before its token -- with LDS atomics, since only counts matter
-// here -- the padded segment offsets (scan over experts), and from these the
-// rows of its K entries: start of the expert's segment + entries of that
-// expert before the token + earlier k of the token with the same expert.  This
-// is the same stable (t*K+k) order the multi-kernel layout produces.  Then it
-// scatters (bf16) or quantises and scatters (FP8) its slice.
-//
-// Shared outputs are split across workgroups: chunk 0 of each token writes its
-// entries' pos, src and recv_w; workgroup 0 writes the per-expert and per-rank
-// outputs and the status; every workgroup marks its share of padding rows.
-// S*K is at most 4096, so each workgroup reads at most 16 KB of routing.
+// A workgroup owns one token (or one slice of its row, for very wide rows):
+// wave 0 plus D data waves, each data lane 16 channels (FP8) or 8 (bf16).
+//   1. Every wave requests what it reads -- the data waves their row slice,
+//      every wave a share of the S*K routing entries, wave 0 the token's K
+//      expert ids and weights -- and clears a share of the LDS counters.
+//   2. Every wave counts its routing share into one packed LDS counter per
+//      expert (low half: all entries, high half: entries before this token;
+//      LDS atomics, since only counts matter here); the data waves then
+//      quantise (FP8) their slice while the counts settle.
+//   3. Wave 0 alone turns the counts into padded segment offsets (one DPP scan
+//      over experts) and the token's K rows: segment start + entries of that
+//      expert before the token + earlier k of the token with the same expert,
+//      the same stable t*K+k order the layout kernels produce.
+//   4. The data waves scatter their slice to the K rows; wave 0 writes the
+//      token's pos, src and recv_w (first slice), the per-expert / per-rank
+//      outputs and the status (workgroup 0), and its share of src = -1 on
+//      padding rows.
+// Three workgroup barriers separate the steps.  Counting runs on every wave
+// because one wave's LDS atomics issue several times slower than the same
+// number spread over the CU's four SIMDs.
 #include "moe_kernels.h"
 
 namespace moe {
 namespace {
 
-constexpr int kT = kFusedDispatchThreads;
-constexpr int kTW = kT / kWave;
-constexpr int kPerThread = kFusedDispatchMaxN / kT;  // routing entries per thread, at most
+// Data waves per workgroup: 4 (at most 4,096 channels of an FP8 row, 2,048 of a
+// bf16 row, per workgroup) measured fastest at the decode shape on MI355X
+// (7 or 3 data waves were 0.15-0.5 us slower per launch); at least 3, so a
+// workgroup has 256 threads to share the routing entries.
+constexpr int kDataWaves = 4;
+constexpr int kMinDataWaves = 3;
+constexpr int kMaxShare = kFusedDispatchMaxN / ((kMinDataWaves + 1) * kWave);  // routing entries per thread
 
-struct SmallLayoutLds {
-    int cnt[kMaxE];       // entries per expert, all tokens
-    int pre[kMaxE];       // entries per expert before this workgroup's token
-    int off[kMaxE + 1];   // first row of each padded segment
-    int pex[kMaxE + 1];   // placed rows before each expert
-    int2 tmp[kTW];
-    int flags;
+struct FusedLds {
+    unsigned int cnt[kMaxE];  // per expert: entries (low 16 bits), entries before the token (high 16)
+    int off[kMaxE + 1];       // first row of each padded segment
+    int pex[kMaxE + 1];       // placed rows before each expert
+    int rows[kMaxK];          // rows of the token's K entries (-1: not placed)
 };
 
-// This thread's routing entries (tid, tid + kT, ...), all loads in flight
-// at once; entries past N read as 0 and are skipped by small_layout.
-__device__ __forceinline__ void load_routing(const LayoutArgs &a, int (&ev)[kPerThread]) {
-#pragma unroll
-    for (int u = 0; u < kPerThread; ++u) {
-        const int i = threadIdx.x + u * kT;
-        ev[u] = i < a.N ? a.idx[i] : 0;
-    }
+// Orders this wave's LDS accesses in the compiler's view; the hardware already
+// runs one wave's LDS instructions in issue order.
+__device__ __forceinline__ void wave_lds_order() {
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    __builtin_amdgcn_wave_barrier();
 }
 
-// Counts, padded offsets, count-only outputs (workgroup 0) and this
-// workgroup's share of padding rows, from load_routing's values.  Returns this
-// thread's flags.
-__device__ int small_layout(const LayoutArgs &a, int t, int K, const int (&ev)[kPerThread], SmallLayoutLds &L) {
-    const int tid = threadIdx.x;
-    for (int e = tid; e < a.E; e += kT) {
-        L.cnt[e] = 0;
-        L.pre[e] = 0;
-    }
-    __syncthreads();
-    int flags = 0;
-    const int before = t * K;
-#pragma unroll
-    for (int u = 0; u < kPerThread; ++u) {
-        const int i = tid + u * kT;
-        if (i >= a.N) break;
-        const int e = ev[u];
-        if (e < 0 || e >= a.E) {
-            flags |= FLAG_BAD_EXPERT;
-            continue;
+// Segment rows and placed rows of an expert with c entries; sets
+// FLAG_CAPACITY in flags on overflow.
+__device__ __forceinline__ int2 segment(const LayoutArgs &a, int c, int &flags) {
+    int seg = c, placed = c;
+    if (a.pad_mode == PAD_MULTIPLE) {
+        seg = (c + a.pad_rows - 1) / a.pad_rows * a.pad_rows;
+    } else if (a.pad_mode == PAD_CAPACITY) {
+        seg = a.pad_rows;
+        if (c > a.pad_rows) {
+            placed = a.pad_rows;
+            flags |= FLAG_CAPACITY;
         }
-        atomicAdd(&L.cnt[e], 1);
-        if (i < before) atomicAdd(&L.pre[e], 1);
     }
-    __syncthreads();
+    return make_int2(seg, placed);
+}
 
-    // thread tid owns experts [tid*ept, tid*ept + ept)
-    const int ept = (a.E + kT - 1) / kT;
-    const int e0 = tid * ept;
-    int seg_sum = 0, placed_sum = 0;
-    for (int j = 0; j < ept && e0 + j < a.E; ++j) {
-        const int c = L.cnt[e0 + j];
-        int seg = c, placed = c;
-        if (a.pad_mode == PAD_MULTIPLE) {
-            seg = (c + a.pad_rows - 1) / a.pad_rows * a.pad_rows;
-        } else if (a.pad_mode == PAD_CAPACITY) {
-            seg = a.pad_rows;
-            if (c > a.pad_rows) { placed = a.pad_rows; flags |= FLAG_CAPACITY; }
+// Step 3 (wave 0): offsets into LDS (and, workgroup 0, tpe / eoff), the
+// token's rows into L.rows.  `my_e` is lane k's expert id for k < K.
+template <int K>
+__device__ __forceinline__ int layout_wave(const LayoutArgs &a, int lane, int my_e, FusedLds &L) {
+    constexpr int kMaxEpt = kMaxE / kWave;
+    const int ept = (a.E + kWave - 1) / kWave;  // lane owns experts [lane*ept, lane*ept + ept)
+    const int e0 = lane * ept;
+    int flags = 0;
+    int c[kMaxEpt];
+    int2 sum = make_int2(0, 0);
+#pragma unroll
+    for (int j = 0; j < kMaxEpt; ++j) {
+        c[j] = (j < ept && e0 + j < a.E) ? static_cast<int>(L.cnt[e0 + j] & 0xFFFFu) : 0;
+        if (j < ept && e0 + j < a.E) {
+            const int2 s = segment(a, c[j], flags);
+            sum.x += s.x;
+            sum.y += s.y;
         }
-        seg_sum += seg;
-        placed_sum += placed;
     }
-    int2 total;
-    const int2 ex = block_exclusive_scan2<kTW>(make_int2(seg_sum, placed_sum), L.tmp, total);
-    const bool write_outputs = blockIdx.x == 0;
-    int so = ex.x, sp = ex.y;
-    for (int j = 0; j < ept && e0 + j < a.E; ++j) {
-        const int e = e0 + j;
-        const int c = L.cnt[e];
-        int seg = c, placed = c;
-        if (a.pad_mode == PAD_MULTIPLE) {
-            seg = (c + a.pad_rows - 1) / a.pad_rows * a.pad_rows;
-        } else if (a.pad_mode == PAD_CAPACITY) {
-            seg = a.pad_rows;
-            placed = c > a.pad_rows ? a.pad_rows : c;
+    const int2 inc = wave_inclusive_scan2(sum);
+    const bool wg0 = blockIdx.x == 0;
+    int so = inc.x - sum.x, sp = inc.y - sum.y;
+#pragma unroll
+    for (int j = 0; j < kMaxEpt; ++j) {
+        if (j < ept && e0 + j < a.E) {
+            const int e = e0 + j;
+            int unused = 0;
+            const int2 s = segment(a, c[j], unused);
+            L.off[e] = so;
+            L.pex[e] = sp;
+            if (wg0) {
+                a.tpe[e] = s.y;
+                a.eoff[e] = so;
+            }
+            so += s.x;
+            sp += s.y;
         }
-        L.off[e] = so;
-        L.pex[e] = sp;
-        if (write_outputs) {
-            a.tpe[e] = placed;
-            a.eoff[e] = so;
-        }
-        so += seg;
-        sp += placed;
     }
-    if (tid == 0) {
-        L.off[a.E] = total.x;
-        L.pex[a.E] = total.y;
-        if (write_outputs) a.eoff[a.E] = total.x;
+    if (lane == kWave - 1) {
+        L.off[a.E] = inc.x;
+        L.pex[a.E] = inc.y;
+        if (wg0) a.eoff[a.E] = inc.x;
     }
-    __syncthreads();
-    if (write_outputs) {
-        const int epr = a.E / a.R;
-        for (int r = tid; r < a.R; r += kT) {
-            a.roff[r] = L.off[r * epr];
-            a.tpr[r] = L.pex[(r + 1) * epr] - L.pex[r * epr];
-        }
-        if (tid == 0) a.roff[a.R] = L.off[a.E];
+    wave_lds_order();
+
+    // lane k < K: row of the token's entry k
+    int within_tok = 0;
+#pragma unroll
+    for (int j = 0; j < K; ++j) {
+        const int ej = __builtin_amdgcn_readlane(my_e, j);
+        within_tok += (j < lane && ej == my_e) ? 1 : 0;
     }
-    const int part = blockIdx.x, parts = gridDim.x;
-    const int wave = tid / kWave, lane = tid & (kWave - 1);
-    for (int e = part + wave * parts; e < a.E; e += kTW * parts) {
-        const int beg = L.off[e] + (L.pex[e + 1] - L.pex[e]);
-        for (int r = beg + lane; r < L.off[e + 1]; r += kWave) a.src[r] = -1;
+    if (lane < K) {
+        const bool valid = my_e >= 0 && my_e < a.E;
+        const int ek = valid ? my_e : 0;
+        const int within = static_cast<int>(L.cnt[ek] >> 16) + within_tok;
+        const bool placed = valid && !(a.pad_mode == PAD_CAPACITY && within >= a.pad_rows);
+        L.rows[lane] = placed ? L.off[ek] + within : -1;
     }
-    for (int r = L.off[a.E] + part * kT + tid; r < a.max_recv; r += kT * parts) a.src[r] = -1;
     return flags;
 }
 
-// Token t's K expert ids (wave-uniform loads, issued at kernel entry).
+// Wave 0, lane k < K of the token's first slice: pos, src and recv_w of entry k.
 template <int K>
-__device__ __forceinline__ void token_experts(const LayoutArgs &a, int t, int (&e)[K]) {
-#pragma unroll
-    for (int k = 0; k < K; ++k) e[k] = a.idx[static_cast<size_t>(t) * K + k];
-}
-
-// Rows of token t's K entries (-1 if not placed) from its expert ids e.
-// Wave-uniform.
-template <int K>
-__device__ __forceinline__ void token_rows(const LayoutArgs &a, const int (&e)[K], const SmallLayoutLds &L,
-                                           int (&p)[K]) {
-    // all 2K LDS reads first (an invalid id reads expert 0 and is dropped
-    // below), so they are in flight together instead of one after another
-    int pre[K], off[K];
-#pragma unroll
-    for (int k = 0; k < K; ++k) {
-        const int ek = (e[k] >= 0 && e[k] < a.E) ? e[k] : 0;
-        pre[k] = L.pre[ek];
-        off[k] = L.off[ek];
-    }
-#pragma unroll
-    for (int k = 0; k < K; ++k) {
-        int within = pre[k];
-#pragma unroll
-        for (int j = 0; j < k; ++j) within += (e[j] == e[k]) ? 1 : 0;
-        const bool placed = e[k] >= 0 && e[k] < a.E && !(a.pad_mode == PAD_CAPACITY && within >= a.pad_rows);
-        p[k] = placed ? off[k] + within : -1;
-    }
-}
-
-// Route weight of token t's entry threadIdx.x (threads below K of chunk 0,
-// when recv_w is wanted), loaded at kernel entry with the other inputs.
-template <int K>
-__device__ __forceinline__ float token_weight(const DispatchArgs &da, int t, int c) {
-    const bool mine = c == 0 && threadIdx.x < K && da.recv_w != nullptr && da.topk_w != nullptr;
-    return mine ? da.topk_w[static_cast<size_t>(t) * K + threadIdx.x] : 0.0f;
-}
-
-// pos, src and recv_w of token t's entries (chunk 0 only); w = token_weight.
-template <int K>
-__device__ __forceinline__ void write_token_maps(const LayoutArgs &la, const DispatchArgs &da, int t,
-                                                 const int (&p)[K], float w) {
-#pragma unroll
-    for (int k = 0; k < K; ++k) {
-        if (threadIdx.x == k) {
-            const int i = t * K + k;
-            la.pos[i] = p[k];
-            if (p[k] >= 0) {
-                la.src[p[k]] = i;
-                if (da.recv_w != nullptr && da.topk_w != nullptr) da.recv_w[p[k]] = w;
-            }
+__device__ __forceinline__ void write_token_maps(const LayoutArgs &a, const DispatchArgs &da, int t, int lane,
+                                                 float w, const FusedLds &L) {
+    if (lane < K) {
+        const int i = t * K + lane;
+        const int row = L.rows[lane];
+        a.pos[i] = row;
+        if (row >= 0) {
+            a.src[row] = i;
+            if (da.recv_w != nullptr && da.topk_w != nullptr) da.recv_w[row] = w;
         }
     }
 }
 
-template <int K>
-__global__ __launch_bounds__(kT) void k_layout_dispatch_fp8(LayoutArgs la, DispatchArgs da, int nchunk) {
-    __shared__ SmallLayoutLds L;
+// Wave 0, step 4: the per-rank outputs and status (workgroup 0), and this
+// workgroup's share of src = -1 on padding rows.  flags: this workgroup's OR.
+__device__ __forceinline__ void layout_wave_outputs(const LayoutArgs &a, int lane, int flags, const FusedLds &L) {
+    if (blockIdx.x == 0) {
+        const int epr = a.E / a.R;
+        for (int r = lane; r < a.R; r += kWave) {
+            a.roff[r] = L.off[r * epr];
+            a.tpr[r] = L.pex[(r + 1) * epr] - L.pex[r * epr];
+        }
+        if (lane == 0) {
+            a.roff[a.R] = L.off[a.E];
+            a.status[0] = flags;
+        }
+    }
+    const int part = blockIdx.x, parts = gridDim.x;
+    for (int e = part; e < a.E; e += parts) {
+        const int beg = L.off[e] + (L.pex[e + 1] - L.pex[e]);
+        for (int r = beg + lane; r < L.off[e + 1]; r += kWave) a.src[r] = -1;
+    }
+    for (int r = L.off[a.E] + part * kWave + lane; r < a.max_recv; r += kWave * parts) a.src[r] = -1;
+}
+
+// blockDim.x = 64 * (1 + D); grid = S * nchunk.
+template <int K, bool FP8>
+__global__ __launch_bounds__((kDataWaves + 1) * kWave) void k_layout_dispatch(LayoutArgs la, DispatchArgs da,
+                                                                                 int nchunk) {
+    __shared__ FusedLds L;
+    __shared__ int s_flags;
     const int t = blockIdx.x / nchunk, c = blockIdx.x % nchunk;
-    const int n16 = da.H / 16;
-    const int g = c * kT + threadIdx.x;
-    const bool active = g < n16;
-    const u32x4 *__restrict__ hid = static_cast<const u32x4 *>(da.hidden) + static_cast<size_t>(t) * (da.H / 8);
+    const int tid = threadIdx.x, nthr = blockDim.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+    const int lane = tid & (kWave - 1);
+    const int per_chunk = nthr - kWave;                 // data lanes
+    const int g = c * per_chunk + tid - kWave;          // this data lane's 16 (FP8) / 8 (bf16) channels
+    const int ngroups = FP8 ? da.H / 16 : da.H / 8;
+    const bool active = wave > 0 && g < ngroups;
+
+    // step 1: requests first
     u32x4 lo = {0u, 0u, 0u, 0u}, hi = {0u, 0u, 0u, 0u};
     if (active) {
-        lo = hid[2 * g];
-        hi = hid[2 * g + 1];
-    }
-    int ev[kPerThread], e[K];
-    load_routing(la, ev);
-    token_experts<K>(la, t, e);
-    const float w = token_weight<K>(da, t, c);
-    if (threadIdx.x == 0) L.flags = 0;
-    const int flags = small_layout(la, t, K, ev, L);
-    int p[K];
-    token_rows<K>(la, e, L, p);
-    if (c == 0) write_token_maps<K>(la, da, t, p, w);
-
-    float scale;
-    const u32x4 q = quantize16_e4m3(lo, hi, scale);
-    const int nsc = da.H / 128;
-    u32x4 *__restrict__ recv = static_cast<u32x4 *>(da.recv);
-    if (active) {
-#pragma unroll
-        for (int k = 0; k < K; ++k) {
-            if (p[k] >= 0) {
-                __builtin_nontemporal_store(q, recv + static_cast<size_t>(p[k]) * n16 + g);
-                if ((threadIdx.x & 7) == 0) da.recv_scales[static_cast<size_t>(p[k]) * nsc + g / 8] = scale;
-            }
+        if (FP8) {
+            const u32x4 *__restrict__ hid = static_cast<const u32x4 *>(da.hidden) + static_cast<size_t>(t) * (da.H / 8);
+            lo = hid[2 * g];
+            hi = hid[2 * g + 1];
+        } else {
+            lo = static_cast<const u32x4 *>(da.hidden)[static_cast<size_t>(t) * ngroups + g];
         }
     }
-    if (flags) atomicOr(&L.flags, flags);
-    __syncthreads();
-    if (blockIdx.x == 0 && threadIdx.x == 0) la.status[0] = L.flags;
-}
-
-template <int K>
-__global__ __launch_bounds__(kT) void k_layout_dispatch_bf16(LayoutArgs la, DispatchArgs da, int nchunk) {
-    __shared__ SmallLayoutLds L;
-    const int t = blockIdx.x / nchunk, c = blockIdx.x % nchunk;
-    const int nvec = da.H / 8;
-    const int v = c * kT + threadIdx.x;
-    const bool active = v < nvec;
-    const u32x4 *__restrict__ hid = static_cast<const u32x4 *>(da.hidden) + static_cast<size_t>(t) * nvec;
-    u32x4 x = {0u, 0u, 0u, 0u};
-    if (active) x = hid[v];
-    int ev[kPerThread], e[K];
-    load_routing(la, ev);
-    token_experts<K>(la, t, e);
-    const float w = token_weight<K>(da, t, c);
-    if (threadIdx.x == 0) L.flags = 0;
-    const int flags = small_layout(la, t, K, ev, L);
-    int p[K];
-    token_rows<K>(la, e, L, p);
-    if (c == 0) write_token_maps<K>(la, da, t, p, w);
-
-    u32x4 *__restrict__ recv = static_cast<u32x4 *>(da.recv);
-    if (active) {
+    int ev[kMaxShare];
 #pragma unroll
-        for (int k = 0; k < K; ++k)
-            if (p[k] >= 0) __builtin_nontemporal_store(x, recv + static_cast<size_t>(p[k]) * nvec + v);
+    for (int u = 0; u < kMaxShare; ++u) {
+        const int i = tid + u * nthr;
+        ev[u] = i < la.N ? la.idx[i] : 0;
     }
-    if (flags) atomicOr(&L.flags, flags);
+    int my_e = -1;
+    float w = 0.0f;
+    if (wave == 0) {
+        if (lane < K) my_e = la.idx[static_cast<size_t>(t) * K + lane];
+        if (c == 0 && lane < K && da.recv_w != nullptr && da.topk_w != nullptr)
+            w = da.topk_w[static_cast<size_t>(t) * K + lane];
+    }
+    for (int e = tid; e < la.E; e += nthr) L.cnt[e] = 0u;
+    if (tid == 0) s_flags = 0;
     __syncthreads();
-    if (blockIdx.x == 0 && threadIdx.x == 0) la.status[0] = L.flags;
+
+    // step 2: counts
+    const int before = t * K;
+    int flags = 0;
+#pragma unroll
+    for (int u = 0; u < kMaxShare; ++u) {
+        const int i = tid + u * nthr;
+        if (i >= la.N) break;
+        const int e = ev[u];
+        if (e >= 0 && e < la.E)
+            atomicAdd(&L.cnt[e], i < before ? 0x10001u : 1u);
+        else
+            flags = FLAG_BAD_EXPERT;
+    }
+    if (__ballot(flags) != 0 && lane == 0) atomicOr(&s_flags, FLAG_BAD_EXPERT);
+    float scale = 0.0f;
+    u32x4 q = {0u, 0u, 0u, 0u};
+    if (wave > 0) {
+        if (FP8) {
+            q = quantize16_e4m3(lo, hi, scale);  // whole data waves: the block max crosses lanes
+        } else {
+            // the row as loaded, in registers of its own: once it has arrived
+            // here no store below waits for a load
+            q = lo;
+            asm volatile("" : "+v"(q));
+        }
+    }
+    __syncthreads();
+
+    // step 3: wave 0 plans
+    if (wave == 0) {
+        flags = layout_wave<K>(la, lane, my_e, L);
+        if (c == 0) write_token_maps<K>(la, da, t, lane, w, L);
+        if (__ballot(flags) != 0 && lane == 0) atomicOr(&s_flags, FLAG_CAPACITY);
+    }
+    __syncthreads();
+
+    // step 4: scatter
+    if (wave == 0) {
+        layout_wave_outputs(la, lane, s_flags, L);
+        return;
+    }
+    if (!active) return;
+    int p[K];
+#pragma unroll
+    for (int k = 0; k < K; ++k) p[k] = L.rows[k];
+    u32x4 *__restrict__ recv = static_cast<u32x4 *>(da.recv);
+    const size_t row_vec = FP8 ? da.H / 16 : da.H / 8;
+    const int nsc = da.H / 128;
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+        if (p[k] >= 0) {
+            __builtin_nontemporal_store(q, recv + static_cast<size_t>(p[k]) * row_vec + g);
+            if (FP8 && (lane & 7) == 0) da.recv_scales[static_cast<size_t>(p[k]) * nsc + g / 8] = scale;
+        }
+    }
 }
 
-#define MOE_FUSED_CASES(KERNEL)                                                              \
-    switch (da.K) {                                                                          \
-        case 1: hipLaunchKernelGGL(KERNEL<1>, grid, block, 0, s, la, da, nchunk); break;     \
-        case 2: hipLaunchKernelGGL(KERNEL<2>, grid, block, 0, s, la, da, nchunk); break;     \
-        case 3: hipLaunchKernelGGL(KERNEL<3>, grid, block, 0, s, la, da, nchunk); break;     \
-        case 4: hipLaunchKernelGGL(KERNEL<4>, grid, block, 0, s, la, da, nchunk); break;     \
-        case 5: hipLaunchKernelGGL(KERNEL<5>, grid, block, 0, s, la, da, nchunk); break;     \
-        case 6: hipLaunchKernelGGL(KERNEL<6>, grid, block, 0, s, la, da, nchunk); break;     \
-        case 7: hipLaunchKernelGGL(KERNEL<7>, grid, block, 0, s, la, da, nchunk); break;     \
-        case 8: hipLaunchKernelGGL(KERNEL<8>, grid, block, 0, s, la, da, nchunk); break;     \
-        case 9: hipLaunchKernelGGL(KERNEL<9>, grid, block, 0, s, la, da, nchunk); break;     \
-        case 10: hipLaunchKernelGGL(KERNEL<10>, grid, block, 0, s, la, da, nchunk); break;   \
-        case 11: hipLaunchKernelGGL(KERNEL<11>, grid, block, 0, s, la, da, nchunk); break;   \
-        case 12: hipLaunchKernelGGL(KERNEL<12>, grid, block, 0, s, la, da, nchunk); break;   \
-        case 13: hipLaunchKernelGGL(KERNEL<13>, grid, block, 0, s, la, da, nchunk); break;   \
-        case 14: hipLaunchKernelGGL(KERNEL<14>, grid, block, 0, s, la, da, nchunk); break;   \
-        case 15: hipLaunchKernelGGL(KERNEL<15>, grid, block, 0, s, la, da, nchunk); break;   \
-        case 16: hipLaunchKernelGGL(KERNEL<16>, grid, block, 0, s, la, da, nchunk); break;   \
-        default: return hipErrorInvalidValue;                                                \
+#define MOE_FUSED_CASES(FP8)                                                                        \
+    switch (da.K) {                                                                                 \
+        case 1: hipLaunchKernelGGL((k_layout_dispatch<1, FP8>), grid, block, 0, s, la, da, nchunk); break;   \
+        case 2: hipLaunchKernelGGL((k_layout_dispatch<2, FP8>), grid, block, 0, s, la, da, nchunk); break;   \
+        case 3: hipLaunchKernelGGL((k_layout_dispatch<3, FP8>), grid, block, 0, s, la, da, nchunk); break;   \
+        case 4: hipLaunchKernelGGL((k_layout_dispatch<4, FP8>), grid, block, 0, s, la, da, nchunk); break;   \
+        case 5: hipLaunchKernelGGL((k_layout_dispatch<5, FP8>), grid, block, 0, s, la, da, nchunk); break;   \
+        case 6: hipLaunchKernelGGL((k_layout_dispatch<6, FP8>), grid, block, 0, s, la, da, nchunk); break;   \
+        case 7: hipLaunchKernelGGL((k_layout_dispatch<7, FP8>), grid, block, 0, s, la, da, nchunk); break;   \
+        case 8: hipLaunchKernelGGL((k_layout_dispatch<8, FP8>), grid, block, 0, s, la, da, nchunk); break;   \
+        case 9: hipLaunchKernelGGL((k_layout_dispatch<9, FP8>), grid, block, 0, s, la, da, nchunk); break;   \
+        case 10: hipLaunchKernelGGL((k_layout_dispatch<10, FP8>), grid, block, 0, s, la, da, nchunk); break; \
+        case 11: hipLaunchKernelGGL((k_layout_dispatch<11, FP8>), grid, block, 0, s, la, da, nchunk); break; \
+        case 12: hipLaunchKernelGGL((k_layout_dispatch<12, FP8>), grid, block, 0, s, la, da, nchunk); break; \
+        case 13: hipLaunchKernelGGL((k_layout_dispatch<13, FP8>), grid, block, 0, s, la, da, nchunk); break; \
+        case 14: hipLaunchKernelGGL((k_layout_dispatch<14, FP8>), grid, block, 0, s, la, da, nchunk); break; \
+        case 15: hipLaunchKernelGGL((k_layout_dispatch<15, FP8>), grid, block, 0, s, la, da, nchunk); break; \
+        case 16: hipLaunchKernelGGL((k_layout_dispatch<16, FP8>), grid, block, 0, s, la, da, nchunk); break; \
+        default: return hipErrorInvalidValue;                                                       \
     }
 
 }  // namespace
 
 hipError_t launch_layout_dispatch_small(const LayoutArgs &la, const DispatchArgs &da, bool fp8, hipStream_t s) {
     const int groups = fp8 ? da.H / 16 : da.H / 8;
-    const int nchunk = (groups + kT - 1) / kT;
-    const dim3 grid(static_cast<unsigned>(da.S) * nchunk), block(kT);
+    int dw = (groups + kWave - 1) / kWave;
+    if (dw > kDataWaves) dw = kDataWaves;
+    if (dw < kMinDataWaves) dw = kMinDataWaves;
+    const int nchunk = (groups + dw * kWave - 1) / (dw * kWave);
+    const dim3 grid(static_cast<unsigned>(da.S) * nchunk), block((dw + 1) * kWave);
     if (fp8) {
-        MOE_FUSED_CASES(k_layout_dispatch_fp8)
+        MOE_FUSED_CASES(true)
     } else {
-        MOE_FUSED_CASES(k_layout_dispatch_bf16)
+        MOE_FUSED_CASES(false)
     }
     return hipGetLastError();
 }

@@ -54,7 +54,6 @@ struct CombineArgs {
 
 // single-launch layout + dispatch for batches of at most this many entries
 constexpr int kFusedDispatchMaxN = 4096;
-constexpr int kFusedDispatchThreads = 256;
 
 // balanced layout: at most this many redundant-expert slots in total (R*B)
 constexpr int kMaxBalanceSlots = 512;
