@@ -13,12 +13,13 @@
 //      expert ids and weights -- and clears a share of the LDS counters.
 //   2. Every wave counts its routing share into one packed LDS counter per
 //      expert (low half: all entries, high half: entries before this token;
-//      LDS atomics, since only counts matter here); the data waves then
-//      quantise (FP8) their slice while the counts settle.
+//      LDS atomics, since only counts matter here).
 //   3. Wave 0 alone turns the counts into padded segment offsets (one DPP scan
 //      over experts) and the token's K rows: segment start + entries of that
 //      expert before the token + earlier k of the token with the same expert,
-//      the same stable t*K+k order the layout kernels produce.
+//      the same stable t*K+k order the layout kernels produce.  Meanwhile the
+//      data waves wait for their row slice and quantise it (FP8), so the plan
+//      overlaps the row loads' latency.
 //   4. The data waves scatter their slice to the K rows; wave 0 writes the
 //      token's pos, src and recv_w (first slice), the per-expert / per-rank
 //      outputs and the status (workgroup 0), and its share of src = -1 on
@@ -37,7 +38,9 @@ namespace {
 // workgroup has 256 threads to share the routing entries.
 constexpr int kDataWaves = 4;
 constexpr int kMinDataWaves = 3;
-constexpr int kMaxShare = kFusedDispatchMaxN / ((kMinDataWaves + 1) * kWave);  // routing entries per thread
+// Routing entries per thread per pass: 8 (every thread's share at the decode
+// shape, 1,024 entries over 320 threads, fits one pass; 4,096 entries take two).
+constexpr int kShare = 8;
 
 struct FusedLds {
     unsigned int cnt[kMaxE];  // per expert: entries (low 16 bits), entries before the token (high 16)
@@ -53,65 +56,79 @@ __device__ __forceinline__ void wave_lds_order() {
     __builtin_amdgcn_wave_barrier();
 }
 
-// Segment rows and placed rows of an expert with c entries; sets
-// FLAG_CAPACITY in flags on overflow.
-__device__ __forceinline__ int2 segment(const LayoutArgs &a, int c, int &flags) {
-    int seg = c, placed = c;
-    if (a.pad_mode == PAD_MULTIPLE) {
-        seg = (c + a.pad_rows - 1) / a.pad_rows * a.pad_rows;
-    } else if (a.pad_mode == PAD_CAPACITY) {
-        seg = a.pad_rows;
-        if (c > a.pad_rows) {
-            placed = a.pad_rows;
-            flags |= FLAG_CAPACITY;
-        }
+// Routing entries first, first + n, ..., first + (kShare-1)*n (0 past N).
+__device__ __forceinline__ void load_share(const LayoutArgs &a, int first, int n, int (&ev)[kShare]) {
+#pragma unroll
+    for (int u = 0; u < kShare; ++u) {
+        const int i = first + u * n;
+        ev[u] = i < a.N ? a.idx[i] : 0;
     }
-    return make_int2(seg, placed);
 }
 
-// Step 3 (wave 0): offsets into LDS (and, workgroup 0, tpe / eoff), the
-// token's rows into L.rows.  `my_e` is lane k's expert id for k < K.
-template <int K>
-__device__ __forceinline__ int layout_wave(const LayoutArgs &a, int lane, int my_e, FusedLds &L) {
-    constexpr int kMaxEpt = kMaxE / kWave;
-    const int ept = (a.E + kWave - 1) / kWave;  // lane owns experts [lane*ept, lane*ept + ept)
-    const int e0 = lane * ept;
+// Segment rows (x) and placed rows (y) of an expert with c entries under pad
+// mode MODE; sets FLAG_CAPACITY in flags on overflow.
+template <int MODE>
+__device__ __forceinline__ int2 segment(int c, int pad_rows, int &flags) {
+    if (MODE == PAD_MULTIPLE) return make_int2((c + pad_rows - 1) / pad_rows * pad_rows, c);
+    if (MODE == PAD_CAPACITY) {
+        if (c > pad_rows) flags |= FLAG_CAPACITY;
+        return make_int2(pad_rows, c > pad_rows ? pad_rows : c);
+    }
+    return make_int2(c, c);
+}
+
+// Step 3, first half (wave 0): the padded offsets of every expert into LDS
+// (and, workgroup 0, tpe / eoff).  Lane l owns experts [l*ept, l*ept + ept).
+// One compact loop per pad mode: a generic body unrolled over every mode and
+// every possible ept ran several times slower (its ~3,000 instructions are
+// fetched once per launch).
+template <int MODE>
+__device__ __forceinline__ int plan_offsets(const LayoutArgs &a, int lane, FusedLds &L) {
+    const int ept = (a.E + kWave - 1) / kWave;
+    const int e0 = min(lane * ept, a.E), e1 = min(e0 + ept, a.E);
     int flags = 0;
-    int c[kMaxEpt];
     int2 sum = make_int2(0, 0);
-#pragma unroll
-    for (int j = 0; j < kMaxEpt; ++j) {
-        c[j] = (j < ept && e0 + j < a.E) ? static_cast<int>(L.cnt[e0 + j] & 0xFFFFu) : 0;
-        if (j < ept && e0 + j < a.E) {
-            const int2 s = segment(a, c[j], flags);
-            sum.x += s.x;
-            sum.y += s.y;
-        }
+#pragma unroll 4
+    for (int e = e0; e < e1; ++e) {
+        const int2 s = segment<MODE>(static_cast<int>(L.cnt[e] & 0xFFFFu), a.pad_rows, flags);
+        sum.x += s.x;
+        sum.y += s.y;
     }
     const int2 inc = wave_inclusive_scan2(sum);
     const bool wg0 = blockIdx.x == 0;
     int so = inc.x - sum.x, sp = inc.y - sum.y;
-#pragma unroll
-    for (int j = 0; j < kMaxEpt; ++j) {
-        if (j < ept && e0 + j < a.E) {
-            const int e = e0 + j;
-            int unused = 0;
-            const int2 s = segment(a, c[j], unused);
-            L.off[e] = so;
-            L.pex[e] = sp;
-            if (wg0) {
-                a.tpe[e] = s.y;
-                a.eoff[e] = so;
-            }
-            so += s.x;
-            sp += s.y;
+#pragma unroll 4
+    for (int e = e0; e < e1; ++e) {
+        int unused = 0;
+        const int2 s = segment<MODE>(static_cast<int>(L.cnt[e] & 0xFFFFu), a.pad_rows, unused);
+        L.off[e] = so;
+        L.pex[e] = sp;
+        if (wg0) {
+            a.tpe[e] = s.y;
+            a.eoff[e] = so;
         }
+        so += s.x;
+        sp += s.y;
     }
     if (lane == kWave - 1) {
         L.off[a.E] = inc.x;
         L.pex[a.E] = inc.y;
         if (wg0) a.eoff[a.E] = inc.x;
     }
+    return flags;
+}
+
+// Step 3 (wave 0): offsets into LDS (and, workgroup 0, tpe / eoff), the
+// token's rows into L.rows.  `my_e` is lane k's expert id for k < K.
+template <int K>
+__device__ __forceinline__ int layout_wave(const LayoutArgs &a, int lane, int my_e, FusedLds &L) {
+    int flags;
+    if (a.pad_mode == PAD_CAPACITY)
+        flags = plan_offsets<PAD_CAPACITY>(a, lane, L);
+    else if (a.pad_mode == PAD_MULTIPLE)
+        flags = plan_offsets<PAD_MULTIPLE>(a, lane, L);
+    else
+        flags = plan_offsets<PAD_NONE>(a, lane, L);
     wave_lds_order();
 
     // lane k < K: row of the token's entry k
@@ -194,12 +211,8 @@ __global__ __launch_bounds__((kDataWaves + 1) * kWave) void k_layout_dispatch(La
             lo = static_cast<const u32x4 *>(da.hidden)[static_cast<size_t>(t) * ngroups + g];
         }
     }
-    int ev[kMaxShare];
-#pragma unroll
-    for (int u = 0; u < kMaxShare; ++u) {
-        const int i = tid + u * nthr;
-        ev[u] = i < la.N ? la.idx[i] : 0;
-    }
+    int ev[kShare];
+    load_share(la, tid, nthr, ev);
     int my_e = -1;
     float w = 0.0f;
     if (wave == 0) {
@@ -214,36 +227,40 @@ __global__ __launch_bounds__((kDataWaves + 1) * kWave) void k_layout_dispatch(La
     // step 2: counts
     const int before = t * K;
     int flags = 0;
+    for (int base = tid;;) {
 #pragma unroll
-    for (int u = 0; u < kMaxShare; ++u) {
-        const int i = tid + u * nthr;
-        if (i >= la.N) break;
-        const int e = ev[u];
-        if (e >= 0 && e < la.E)
-            atomicAdd(&L.cnt[e], i < before ? 0x10001u : 1u);
-        else
-            flags = FLAG_BAD_EXPERT;
+        for (int u = 0; u < kShare; ++u) {
+            const int i = base + u * nthr;
+            const int e = ev[u];
+            if (i < la.N) {
+                if (e >= 0 && e < la.E)
+                    atomicAdd(&L.cnt[e], i < before ? 0x10001u : 1u);
+                else
+                    flags = FLAG_BAD_EXPERT;
+            }
+        }
+        base += kShare * nthr;
+        if (base - tid >= la.N) break;
+        load_share(la, base, nthr, ev);
     }
     if (__ballot(flags) != 0 && lane == 0) atomicOr(&s_flags, FLAG_BAD_EXPERT);
-    float scale = 0.0f;
-    u32x4 q = {0u, 0u, 0u, 0u};
-    if (wave > 0) {
-        if (FP8) {
-            q = quantize16_e4m3(lo, hi, scale);  // whole data waves: the block max crosses lanes
-        } else {
-            // the row as loaded, in registers of its own: once it has arrived
-            // here no store below waits for a load
-            q = lo;
-            asm volatile("" : "+v"(q));
-        }
-    }
     __syncthreads();
 
-    // step 3: wave 0 plans
+    // step 3: wave 0 plans while the data waves wait for their rows and
+    // quantise them
+    float scale = 0.0f;
+    u32x4 q = {0u, 0u, 0u, 0u};
     if (wave == 0) {
         flags = layout_wave<K>(la, lane, my_e, L);
         if (c == 0) write_token_maps<K>(la, da, t, lane, w, L);
         if (__ballot(flags) != 0 && lane == 0) atomicOr(&s_flags, FLAG_CAPACITY);
+    } else if (FP8) {
+        q = quantize16_e4m3(lo, hi, scale);  // whole data waves: the block max crosses lanes
+    } else {
+        // the row as loaded, in registers of its own: once it has arrived
+        // here no store below waits for a load
+        q = lo;
+        asm volatile("" : "+v"(q));
     }
     __syncthreads();
 
