@@ -28,6 +28,7 @@
 // because one wave's LDS atomics issue several times slower than the same
 // number spread over the CU's four SIMDs.
 #include "moe_kernels.h"
+#include "small_layout.h"
 
 namespace moe {
 namespace {
@@ -35,101 +36,20 @@ namespace {
 // Data waves per workgroup: 4 (at most 4,096 channels of an FP8 row, 2,048 of a
 // bf16 row, per workgroup) measured fastest at the decode shape on MI355X
 // (7 or 3 data waves were 0.15-0.5 us slower per launch); at least 3, so a
-// workgroup has 256 threads to share the routing entries.
+// workgroup has 256 threads to share the routing entries (at the decode shape
+// 1,024 entries: one counting pass per thread).
 constexpr int kDataWaves = 4;
 constexpr int kMinDataWaves = 3;
-// Routing entries per thread per pass: 8 (every thread's share at the decode
-// shape, 1,024 entries over 320 threads, fits one pass; 4,096 entries take two).
-constexpr int kShare = 8;
 
-struct FusedLds {
-    unsigned int cnt[kMaxE];  // per expert: entries (low 16 bits), entries before the token (high 16)
-    int off[kMaxE + 1];       // first row of each padded segment
-    int pex[kMaxE + 1];       // placed rows before each expert
-    int rows[kMaxK];          // rows of the token's K entries (-1: not placed)
+struct FusedLds : small::Counts {
+    int rows[kMaxK];  // rows of the token's K entries (-1: not placed)
 };
-
-// Orders this wave's LDS accesses in the compiler's view; the hardware already
-// runs one wave's LDS instructions in issue order.
-__device__ __forceinline__ void wave_lds_order() {
-    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-}
-
-// Routing entries first, first + n, ..., first + (kShare-1)*n (0 past N).
-__device__ __forceinline__ void load_share(const LayoutArgs &a, int first, int n, int (&ev)[kShare]) {
-#pragma unroll
-    for (int u = 0; u < kShare; ++u) {
-        const int i = first + u * n;
-        ev[u] = i < a.N ? a.idx[i] : 0;
-    }
-}
-
-// Segment rows (x) and placed rows (y) of an expert with c entries under pad
-// mode MODE; sets FLAG_CAPACITY in flags on overflow.
-template <int MODE>
-__device__ __forceinline__ int2 segment(int c, int pad_rows, int &flags) {
-    if (MODE == PAD_MULTIPLE) return make_int2((c + pad_rows - 1) / pad_rows * pad_rows, c);
-    if (MODE == PAD_CAPACITY) {
-        if (c > pad_rows) flags |= FLAG_CAPACITY;
-        return make_int2(pad_rows, c > pad_rows ? pad_rows : c);
-    }
-    return make_int2(c, c);
-}
-
-// Step 3, first half (wave 0): the padded offsets of every expert into LDS
-// (and, workgroup 0, tpe / eoff).  Lane l owns experts [l*ept, l*ept + ept).
-// One compact loop per pad mode: a generic body unrolled over every mode and
-// every possible ept ran several times slower (its ~3,000 instructions are
-// fetched once per launch).
-template <int MODE>
-__device__ __forceinline__ int plan_offsets(const LayoutArgs &a, int lane, FusedLds &L) {
-    const int ept = (a.E + kWave - 1) / kWave;
-    const int e0 = min(lane * ept, a.E), e1 = min(e0 + ept, a.E);
-    int flags = 0;
-    int2 sum = make_int2(0, 0);
-#pragma unroll 4
-    for (int e = e0; e < e1; ++e) {
-        const int2 s = segment<MODE>(static_cast<int>(L.cnt[e] & 0xFFFFu), a.pad_rows, flags);
-        sum.x += s.x;
-        sum.y += s.y;
-    }
-    const int2 inc = wave_inclusive_scan2(sum);
-    const bool wg0 = blockIdx.x == 0;
-    int so = inc.x - sum.x, sp = inc.y - sum.y;
-#pragma unroll 4
-    for (int e = e0; e < e1; ++e) {
-        int unused = 0;
-        const int2 s = segment<MODE>(static_cast<int>(L.cnt[e] & 0xFFFFu), a.pad_rows, unused);
-        L.off[e] = so;
-        L.pex[e] = sp;
-        if (wg0) {
-            a.tpe[e] = s.y;
-            a.eoff[e] = so;
-        }
-        so += s.x;
-        sp += s.y;
-    }
-    if (lane == kWave - 1) {
-        L.off[a.E] = inc.x;
-        L.pex[a.E] = inc.y;
-        if (wg0) a.eoff[a.E] = inc.x;
-    }
-    return flags;
-}
 
 // Step 3 (wave 0): offsets into LDS (and, workgroup 0, tpe / eoff), the
 // token's rows into L.rows.  `my_e` is lane k's expert id for k < K.
 template <int K>
 __device__ __forceinline__ int layout_wave(const LayoutArgs &a, int lane, int my_e, FusedLds &L) {
-    int flags;
-    if (a.pad_mode == PAD_CAPACITY)
-        flags = plan_offsets<PAD_CAPACITY>(a, lane, L);
-    else if (a.pad_mode == PAD_MULTIPLE)
-        flags = plan_offsets<PAD_MULTIPLE>(a, lane, L);
-    else
-        flags = plan_offsets<PAD_NONE>(a, lane, L);
-    wave_lds_order();
+    const int flags = small::plan_offsets(a, lane, L);
 
     // lane k < K: row of the token's entry k
     int within_tok = 0;
@@ -163,28 +83,6 @@ __device__ __forceinline__ void write_token_maps(const LayoutArgs &a, const Disp
     }
 }
 
-// Wave 0, step 4: the per-rank outputs and status (workgroup 0), and this
-// workgroup's share of src = -1 on padding rows.  flags: this workgroup's OR.
-__device__ __forceinline__ void layout_wave_outputs(const LayoutArgs &a, int lane, int flags, const FusedLds &L) {
-    if (blockIdx.x == 0) {
-        const int epr = a.E / a.R;
-        for (int r = lane; r < a.R; r += kWave) {
-            a.roff[r] = L.off[r * epr];
-            a.tpr[r] = L.pex[(r + 1) * epr] - L.pex[r * epr];
-        }
-        if (lane == 0) {
-            a.roff[a.R] = L.off[a.E];
-            a.status[0] = flags;
-        }
-    }
-    const int part = blockIdx.x, parts = gridDim.x;
-    for (int e = part; e < a.E; e += parts) {
-        const int beg = L.off[e] + (L.pex[e + 1] - L.pex[e]);
-        for (int r = beg + lane; r < L.off[e + 1]; r += kWave) a.src[r] = -1;
-    }
-    for (int r = L.off[a.E] + part * kWave + lane; r < a.max_recv; r += kWave * parts) a.src[r] = -1;
-}
-
 // blockDim.x = 64 * (1 + D); grid = S * nchunk.
 template <int K, bool FP8>
 __global__ __launch_bounds__((kDataWaves + 1) * kWave) void k_layout_dispatch(LayoutArgs la, DispatchArgs da,
@@ -211,8 +109,8 @@ __global__ __launch_bounds__((kDataWaves + 1) * kWave) void k_layout_dispatch(La
             lo = static_cast<const u32x4 *>(da.hidden)[static_cast<size_t>(t) * ngroups + g];
         }
     }
-    int ev[kShare];
-    load_share(la, tid, nthr, ev);
+    int ev[small::kShare];
+    small::load_share(la, tid, nthr, ev);
     int my_e = -1;
     float w = 0.0f;
     if (wave == 0) {
@@ -220,29 +118,12 @@ __global__ __launch_bounds__((kDataWaves + 1) * kWave) void k_layout_dispatch(La
         if (c == 0 && lane < K && da.recv_w != nullptr && da.topk_w != nullptr)
             w = da.topk_w[static_cast<size_t>(t) * K + lane];
     }
-    for (int e = tid; e < la.E; e += nthr) L.cnt[e] = 0u;
+    small::clear(la, tid, nthr, L);
     if (tid == 0) s_flags = 0;
     __syncthreads();
 
     // step 2: counts
-    const int before = t * K;
-    int flags = 0;
-    for (int base = tid;;) {
-#pragma unroll
-        for (int u = 0; u < kShare; ++u) {
-            const int i = base + u * nthr;
-            const int e = ev[u];
-            if (i < la.N) {
-                if (e >= 0 && e < la.E)
-                    atomicAdd(&L.cnt[e], i < before ? 0x10001u : 1u);
-                else
-                    flags = FLAG_BAD_EXPERT;
-            }
-        }
-        base += kShare * nthr;
-        if (base - tid >= la.N) break;
-        load_share(la, base, nthr, ev);
-    }
+    int flags = small::count(la, tid, nthr, t * K, ev, L);
     if (__ballot(flags) != 0 && lane == 0) atomicOr(&s_flags, FLAG_BAD_EXPERT);
     __syncthreads();
 
@@ -266,7 +147,7 @@ __global__ __launch_bounds__((kDataWaves + 1) * kWave) void k_layout_dispatch(La
 
     // step 4: scatter
     if (wave == 0) {
-        layout_wave_outputs(la, lane, s_flags, L);
+        small::write_outputs(la, lane, s_flags, L);
         return;
     }
     if (!active) return;

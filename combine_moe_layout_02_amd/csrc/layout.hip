@@ -16,7 +16,9 @@
 // A column scan over the 16 per-wave counters then orders the waves.  Nothing
 // depends on the order in which waves or workgroups run.
 //
-// Three variants (thresholds measured on MI355X):
+// Four variants (thresholds measured on MI355X):
+//   small  (S*K <= 4096 and E > 64): 64 workgroups, each recounting every
+//          entry with LDS atomics and placing 64 of them (k_layout_small).
 //   single (S*K <= 2048): one 1024-thread workgroup does everything in one
 //          launch.  Above that one CU cannot issue the scattered src stores
 //          fast enough.
@@ -29,6 +31,7 @@
 //          histograms -- cheaper than a separate scan launch -- and turns tile
 //          ranks into rows.  Small tiles spread the scatter over more CUs.
 #include "moe_kernels.h"
+#include "small_layout.h"
 
 namespace moe {
 namespace {
@@ -124,6 +127,54 @@ __global__ __launch_bounds__(kLayoutThreads) void k_layout_fused(LayoutArgs a) {
     if (flags) atomicOr(&s_flags, flags);
     __syncthreads();
     if (tid == 0) a.status[0] = s_flags;
+}
+
+// Small batches (S*K <= 4096, more than 64 experts): 64 workgroups of 256
+// threads, workgroup b owning entries [64b, 64b + 64), so the scattered pos /
+// src stores and the padding rows' src = -1 spread over 64 CUs.  All four
+// waves recount every entry into packed counters (all entries / entries
+// before this workgroup's first), then wave 0 scans them into padded offsets
+// and places its 64 entries: row = segment start + entries of that expert
+// before this workgroup + lanes below with the same expert (one ballot per key
+// bit), the stable t*K+k order.  Workgroup 0 writes the count outputs and the
+// status; every workgroup marks its share of padding rows.  64 workgroups even
+// for a few entries: at fixed capacity a decode batch has ~31,000 padding rows
+// to mark, and fewer workgroups took longer (16: +0.7 us, 1: +24 us).
+constexpr int kSmallMinE = 64;  // with fewer experts the single workgroup measured faster
+constexpr int kSmallThreads = 256;
+constexpr int kSmallBlocks = small::kMaxN / kWave;
+
+__global__ __launch_bounds__(kSmallThreads) void k_layout_small(LayoutArgs a) {
+    __shared__ small::Counts L;
+    __shared__ int s_flags;
+    const int tid = threadIdx.x, lane = tid & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+    const int first = blockIdx.x * kWave;  // this workgroup's entries: [first, first + 64)
+    int ev[small::kShare];
+    small::load_share(a, tid, kSmallThreads, ev);
+    const int i = first + lane;
+    const int mine = (wave == 0 && i < a.N) ? a.idx[i] : -1;
+    small::clear(a, tid, kSmallThreads, L);
+    if (tid == 0) s_flags = 0;
+    __syncthreads();
+
+    const int bad = small::count(a, tid, kSmallThreads, first, ev, L);
+    if (__ballot(bad) != 0 && lane == 0) atomicOr(&s_flags, FLAG_BAD_EXPERT);
+    __syncthreads();
+    if (wave != 0) return;
+
+    const int cap = small::plan_offsets(a, lane, L);
+    const bool in = i < a.N;
+    const bool ok = in && mine >= 0 && mine < a.E;
+    const uint64_t m = match_key(mine, ok, a.nbits);
+    const int within = ok ? static_cast<int>(L.cnt[mine] >> 16) + lanes_below(m) : 0;
+    const bool placed = ok && !(a.pad_mode == PAD_CAPACITY && within >= a.pad_rows);
+    const int row = placed ? L.off[mine] + within : -1;
+    if (in) {
+        a.pos[i] = row;
+        if (row >= 0) a.src[row] = i;
+    }
+    small::write_outputs(a, lane, s_flags | (__ballot(cap) != 0 ? FLAG_CAPACITY : 0), L);
 }
 
 template <int J>
@@ -273,6 +324,11 @@ hipError_t launch_onepass(const LayoutArgs &a, size_t lds, hipStream_t s) {
     return hipGetLastError();
 }
 
+hipError_t launch_small(const LayoutArgs &a, hipStream_t s) {
+    hipLaunchKernelGGL(k_layout_small, dim3(kSmallBlocks), dim3(kSmallThreads), 0, s, a);
+    return hipGetLastError();
+}
+
 template <int J>
 hipError_t launch_fused(const LayoutArgs &a, size_t lds, hipStream_t s) {
     hipLaunchKernelGGL(k_layout_fused<J>, dim3(1), dim3(kLayoutThreads), lds, s, a);
@@ -303,6 +359,7 @@ hipError_t launch_multi(LayoutArgs a, size_t lds, hipStream_t s) {
 
 hipError_t launch_layout(const LayoutArgs &a, hipStream_t s) {
     const size_t lds = static_cast<size_t>(kLayoutWaves) * a.E * sizeof(unsigned short);
+    if (a.N <= small::kMaxN && a.E > kSmallMinE) return launch_small(a, s);
     if (a.N <= kSingleMaxN) {
         if (a.N <= kLayoutThreads) return launch_fused<1>(a, lds, s);
         return launch_fused<2>(a, lds, s);

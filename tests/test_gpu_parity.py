@@ -126,6 +126,12 @@ EDGE = [
     (_case("tiles-4096-E96-R3", 37500, 8, 96, 8, 3, PAD_MULTIPLE, 5), False, None, False),
     # 2048-entry tiles with a capacity that some experts exceed
     (_case("tiles-2048-capacity", 20000, 16, 40, 5, 5, PAD_CAPACITY, 2500), False, None, False),
+    # boundaries of the small-batch layout (S*K <= 4096 and more than 64 experts)
+    (_case("small-E65-N4096", 4096, 64, 65, 1, 5), False, None, False),
+    (_case("single-E64-N2048", 256, 64, 64, 8, 8), False, None, False),
+    (_case("onepass-N4097-E128", 4097, 64, 128, 1, 8, PAD_MULTIPLE, 3), False, None, False),
+    (_case("small-capacity-overflow", 400, 128, 128, 8, 8, PAD_CAPACITY, 20), True, None, False),
+    (_case("small-bad-ids", 200, 64, 96, 4, 4, PAD_MULTIPLE, 16), False, "bad", True),
 ]
 
 
@@ -197,16 +203,18 @@ def dataclasses_replace_uniform(cfg):
     return dataclasses.replace(cfg, routing="uniform", K=min(cfg.K, cfg.E))
 
 
-def test_empty_batch(moe):
+@pytest.mark.parametrize("E", [8, 256])   # single-workgroup and small-batch layouts
+def test_empty_batch(moe, E):
     for pad_mode, pad_rows in ((PAD_NONE, 0), (PAD_MULTIPLE, 4), (PAD_CAPACITY, 3)):
-        say(f"case empty: pad={pad_mode}/{pad_rows}")
-        desc = moe.LayoutDesc(0, 2, 8, 2, pad_mode, pad_rows)
+        say(f"case empty: E={E} pad={pad_mode}/{pad_rows}")
+        desc = moe.LayoutDesc(0, 2, E, 2, pad_mode, pad_rows)
         idx = torch.empty((0, 2), dtype=torch.int32, device=DEV)
         lay = moe.alloc_layout(desc, DEV)
         lay.status.fill_(-1)
+        lay.src.fill_(7)
         moe.moe_layout(desc, idx, lay)
         torch.cuda.synchronize()
-        compare_layout(lay, oracle.layout(np.zeros((0, 2), np.int32), 8, 2, pad_mode, pad_rows), "empty")
+        compare_layout(lay, oracle.layout(np.zeros((0, 2), np.int32), E, 2, pad_mode, pad_rows), "empty")
         hid = torch.empty((0, 64), dtype=torch.bfloat16, device=DEV)
         moe.moe_dispatch(desc, lay, hid)
         y = torch.zeros((max(moe.moe_max_recv_rows(desc), 1), 64), dtype=torch.bfloat16, device=DEV)
