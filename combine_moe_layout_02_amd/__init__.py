@@ -334,7 +334,7 @@ def moe_layout_balanced(desc: LayoutDesc, slots_per_rank: int, topk_idx: torch.T
 def moe_layout_dispatch(desc: LayoutDesc, topk_idx: torch.Tensor, hidden: torch.Tensor, topk_w=None,
                         fp8: bool = False, layout: Optional[Layout] = None, recv=None, recv_scales=None,
                         recv_w=None, stream=None):
-    """moe_layout + moe_dispatch in one call (one launch for S*K <= 4096).
+    """moe_layout + moe_dispatch in one call (one launch for S*K <= 4096 and S <= 512).
     Returns (layout, recv, recv_scales or None, recv_w or None)."""
     dev = hidden.device
     H = hidden.shape[1]

@@ -43,6 +43,14 @@ int ceil_log2(int x) {
 
 bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
+// moe_layout_dispatch takes its one-launch form up to this many tokens: every
+// workgroup of that form (one per token and row slice) recounts all S*K
+// entries, so its cost grows with S times S*K.  Measured on MI355X at S*K
+// <= 4096: one launch 6.6 / 9.9 us against 7.9 / 12.0 us for layout +
+// dispatch at S = 128 / 512; 12.3 against 11.7 at S = 1024 and 36.6 against
+// 22.9 at S = 4096 (FP8, H = 7168).
+constexpr int kFusedMaxTokens = 512;
+
 }  // namespace
 
 extern "C" {
@@ -168,7 +176,7 @@ moe_status moe_layout_dispatch(const moe_layout_desc *desc, const int32_t *topk_
     da.pos = out->pos;
     const hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t err;
-    if (la.N > 0 && la.N <= moe::kFusedDispatchMaxN) {
+    if (la.N > 0 && la.N <= moe::kFusedDispatchMaxN && desc->S <= kFusedMaxTokens) {
         err = moe::launch_layout_dispatch_small(la, da, fp8 != 0, s);
     } else {
         err = moe::launch_layout(la, s);

@@ -159,9 +159,9 @@ moe_status moe_dispatch(const moe_layout_desc *desc, const moe_layout_bufs *layo
 
 /* Layout + dispatch in one call: the same results as moe_layout followed by
  * moe_dispatch with these arguments (every output of both).  Batches with
- * S*K <= 4096 (decode-sized) run as ONE kernel launch in which each workgroup
- * rebuilds the layout counts it needs in LDS; larger batches run the two calls'
- * kernels back to back.  Arguments as in moe_layout and moe_dispatch; the
+ * S*K <= 4096 and S <= 512 (decode-sized) run as ONE kernel launch in which
+ * each workgroup rebuilds the layout counts it needs in LDS; other batches run
+ * the two calls' kernels back to back.  Arguments as in moe_layout and moe_dispatch; the
  * workspace rule is moe_layout's.  This is the low-latency variant for
  * inference decoding (DeepEP analysis, feature list: low-latency kernels for
  * decoding). */

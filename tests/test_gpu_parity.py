@@ -600,12 +600,15 @@ FUSED = [
     ("bad-ids", 200, 136, 32, 4, 2, PAD_NONE, 0, False, "bad"),
     ("duplicates", 100, 8, 4, 6, 2, PAD_MULTIPLE, 3, False, "dup"),
     ("one-token", 1, 128, 1, 1, 1, PAD_NONE, 0, True, "uniform"),
+    # the one-launch form's token limit (S <= 512) at S*K <= 4096
+    ("fused-S512-N4096", 512, 1024, 256, 8, 8, PAD_CAPACITY, 20, True, "uniform"),
+    ("fallback-S513-N3591", 513, 1024, 128, 7, 8, PAD_MULTIPLE, 4, False, "uniform"),
 ]
 
 
 def _random_fused(n=20, seed=5151):
     """Seeded random decode-sized shapes for moe_layout_dispatch (most within
-    the one-launch limit S*K <= 4096, some just past it)."""
+    S*K <= 4096, some just past it; the one-launch form also needs S <= 512)."""
     rng = np.random.default_rng(seed)
     out = []
     for i in range(n):
@@ -629,8 +632,9 @@ FUSED += _random_fused()
 
 @pytest.mark.parametrize("case", FUSED, ids=[c[0] for c in FUSED])
 def test_layout_dispatch(moe, case):
-    """moe_layout_dispatch (one launch for S*K <= 4096, two otherwise) against
-    the oracle's layout + dispatch, every output bit for bit."""
+    """moe_layout_dispatch (one launch for S*K <= 4096 and S <= 512, two
+    otherwise) against the oracle's layout + dispatch, every output bit for
+    bit."""
     name, S, H, E, K, R, pad_mode, pad_rows, fp8, routing = case
     seed = 7000 + FUSED.index(case)
     rng = np.random.default_rng(seed)
