@@ -420,7 +420,8 @@ __global__ __launch_bounds__(kLayoutThreads) void k_balance_place(BalanceArgs b)
 // entries.  No plain layout is written or read back.
 __global__ __launch_bounds__(kLayoutThreads) void k_layout_balanced_onepass(LayoutArgs a, BalanceArgs b) {
     extern __shared__ unsigned short s_cnt[];  // [kLayoutWaves][E]
-    __shared__ int s_before[kMaxE], s_after[kMaxE];
+    __shared__ int s_before[kMaxE];
+    __shared__ __align__(16) unsigned int s_part[kOtherWords];
     __shared__ BalanceLds L;
     __shared__ int s_bad;
     const int tid = threadIdx.x, wave = tid / kWave, lane = tid & (kWave - 1), tb = blockIdx.x;
@@ -429,10 +430,7 @@ __global__ __launch_bounds__(kLayoutThreads) void k_layout_balanced_onepass(Layo
     int raw[1];
     load_keys<1>(a.idx, a.N, base, raw);
     for (int x = tid; x < kLayoutWaves * E; x += kLayoutThreads) s_cnt[x] = 0;
-    for (int e = tid; e < E; e += kLayoutThreads) {
-        s_before[e] = 0;
-        s_after[e] = 0;
-    }
+    other_clear(s_part, E);
     if (tid == 0) {
         s_bad = 0;
         L.flags = 0;
@@ -440,14 +438,18 @@ __global__ __launch_bounds__(kLayoutThreads) void k_layout_balanced_onepass(Layo
     __syncthreads();
 
     int flags = 0, bad = 0;
-    count_other_tiles(a.idx, a.N, E, nblk, tb, s_before, s_after, flags, bad);
     int key[1], local[1];
-    wave_rank<1>(raw, a.N, E, a.nbits, base, s_cnt + wave * E, key, local, flags);
+    count_other_tiles(a.idx, a.N, E, nblk, tb, s_part, flags, bad,
+                      [&] { wave_rank<1>(raw, a.N, E, a.nbits, base, s_cnt + wave * E, key, local, flags); });
     if (base + lane < a.N && key[0] < 0) ++bad;
     if (flags) atomicOr(&L.flags, flags);
     if (bad) atomicAdd(&s_bad, bad);
     __syncthreads();
-    if (tid < E) L.cnt[tid] = s_before[tid] + column_scan(s_cnt, E, tid) + s_after[tid];
+    if (tid < E) {
+        const unsigned int other = other_total(s_part, E, tid);
+        s_before[tid] = static_cast<int>(other >> 16);
+        L.cnt[tid] = column_scan(s_cnt, E, tid) + static_cast<int>(other & 0xFFFFu);
+    }
     __syncthreads();
     plan_balance(L, E, b.R, b.B, a.N - s_bad);
     if (tb == 0) write_balance_counts(L, b);

@@ -268,15 +268,17 @@ __global__ __launch_bounds__(kLayoutThreads) void k_layout_place(LayoutArgs a) {
 
 // One-launch layout for mid-sized batches (tiles of 1024 entries, one
 // workgroup each).  Workgroup b ranks its own tile as k_layout_local does and
-// counts every other tile's entries itself (LDS atomics into "before b" and
-// "after b" counters), so without any exchange between workgroups it knows
-// the per-expert totals and the entries of earlier tiles; then it places its
-// tile as k_layout_place does.  The redundant counting costs one coalesced
-// load per thread per tile, served from L2 once the first workgroups have
-// touched topk_idx.
+// counts every other tile's entries itself (count_other_tiles: one packed
+// counter per expert, entries of all other tiles and of the tiles before b),
+// so without any exchange between workgroups it knows the per-expert totals
+// and the entries of earlier tiles; then it places its tile as k_layout_place
+// does.  The redundant counting costs one 16-byte load per thread per four
+// tiles, served from L2 once the first workgroups have touched topk_idx, and
+// one LDS atomic per entry; the own tile is ranked while those loads are out.
 __global__ __launch_bounds__(kLayoutThreads) void k_layout_onepass(LayoutArgs a) {
     extern __shared__ unsigned short s_cnt[];  // [kLayoutWaves][E]
-    __shared__ int s_off[kMaxE + 1], s_pex[kMaxE + 1], s_before[kMaxE], s_after[kMaxE];
+    __shared__ int s_off[kMaxE + 1], s_pex[kMaxE + 1], s_before[kMaxE];
+    __shared__ __align__(16) unsigned int s_part[kOtherWords];
     __shared__ int2 s_tmp[kLayoutWaves];
     __shared__ int s_flags;
     const int tid = threadIdx.x, wave = tid / kWave, lane = tid & (kWave - 1), b = blockIdx.x;
@@ -285,19 +287,21 @@ __global__ __launch_bounds__(kLayoutThreads) void k_layout_onepass(LayoutArgs a)
     int raw[1];
     load_keys<1>(a.idx, a.N, base, raw);
     for (int x = tid; x < kLayoutWaves * a.E; x += kLayoutThreads) s_cnt[x] = 0;
-    for (int e = tid; e < a.E; e += kLayoutThreads) {
-        s_before[e] = 0;
-        s_after[e] = 0;
-    }
+    other_clear(s_part, a.E);
     if (tid == 0) s_flags = 0;
     __syncthreads();
 
     int flags = 0, bad = 0;
-    count_other_tiles(a.idx, a.N, a.E, nblk, b, s_before, s_after, flags, bad);
     int key[1], local[1];
-    wave_rank<1>(raw, a.N, a.E, a.nbits, base, s_cnt + wave * a.E, key, local, flags);
+    count_other_tiles(a.idx, a.N, a.E, nblk, b, s_part, flags, bad,
+                      [&] { wave_rank<1>(raw, a.N, a.E, a.nbits, base, s_cnt + wave * a.E, key, local, flags); });
     __syncthreads();
-    const int cnt = tid < a.E ? column_scan(s_cnt, a.E, tid) + s_before[tid] + s_after[tid] : 0;
+    int cnt = 0;
+    if (tid < a.E) {
+        const unsigned int other = other_total(s_part, a.E, tid);
+        s_before[tid] = static_cast<int>(other >> 16);
+        cnt = column_scan(s_cnt, a.E, tid) + static_cast<int>(other & 0xFFFFu);
+    }
     flags |= finish_counts(a, cnt, s_off, s_pex, s_tmp, b == 0, b, nblk);  // synchronises the workgroup
 
     const int i = base + lane;

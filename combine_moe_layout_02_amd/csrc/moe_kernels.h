@@ -229,48 +229,155 @@ __device__ __forceinline__ void wave_rank(const int (&raw)[J], int N, int E, int
 }
 
 // Per-wave counters of expert e -> exclusive prefixes over waves; returns the
-// workgroup's total for e.
+// workgroup's total for e.  All 16 counters are read before the first write:
+// read, write, read, ... in one loop made the compiler wait for each read in
+// turn (it cannot tell the addresses apart), 16 LDS round trips in a row.
 __device__ __forceinline__ int column_scan(unsigned short *s_cnt, int E, int e) {
+    int c[kLayoutWaves];
+#pragma unroll
+    for (int w = 0; w < kLayoutWaves; ++w) c[w] = s_cnt[w * E + e];
     int run = 0;
 #pragma unroll
     for (int w = 0; w < kLayoutWaves; ++w) {
-        const int c = s_cnt[w * E + e];
         s_cnt[w * E + e] = static_cast<unsigned short>(run);
-        run += c;
+        run += c[w];
     }
     return run;
 }
 
-// Entries of every 1024-entry tile except tile `b` (of nblk), counted per
-// expert into s_before (tiles before b) and s_after (tiles after b) with LDS
-// atomics; entries with an expert outside [0,E) set FLAG_BAD_EXPERT in flags
-// and are added to bad.  16 loads in flight per thread.  Redundant work that
-// lets one workgroup per tile know every count without talking to the others.
-__device__ __forceinline__ void count_other_tiles(const int32_t *__restrict__ idx, int N, int E, int nblk,
-                                                  int b, int *s_before, int *s_after, int &flags, int &bad) {
+// Counts of the other tiles' entries for the one-launch layouts (one
+// workgroup per 1024-entry tile, N <= 65535).  Per expert one packed counter:
+// low 16 bits the entries of every tile but the workgroup's own, high 16 bits
+// those of the tiles before it, so each entry costs one LDS atomic.  The
+// counter has 1 << other_copies_log2(E) copies (8 for E <= 256), copy c taken
+// by the threads with tid % copies == c, which spreads one instruction's
+// atomics over more banks and addresses; other_total sums the copies.  At the
+// prefill shape (32 tiles, E=256) 8 copies counted ~0.3 us faster than one.
+constexpr int kOtherWords = 2048 + 8;  // LDS words of the copies for any E <= kMaxE, plus a spare expert
+static_assert(kOnePassMaxN <= 65535, "other-tile counts are packed in 16 bits");
+__device__ __forceinline__ int other_copies_log2(int E) { return E <= 256 ? 3 : (E <= 512 ? 2 : 1); }
+
+// Zeroes the copies and the spare expert's (every thread of the workgroup;
+// synchronise before counting).
+__device__ __forceinline__ void other_clear(unsigned int *s_part, int E) {
+    for (int x = threadIdx.x; x < ((E + 1) << other_copies_log2(E)); x += kLayoutThreads) s_part[x] = 0u;
+}
+
+// count_other_tiles with 1 << CL copies (a constant, so the counter address is
+// one shift-and-or).  An id outside [0,E) adds one to nbad and is counted into
+// the spare expert E, which nothing reads, so every lane takes part in every
+// atomic and the loop has no branches per entry; slots past N are loaded as -1
+// and taken back out of nbad.
+template <int CL, typename Between>
+__device__ __forceinline__ void count_other_tiles_cl(const int32_t *__restrict__ idx, int N, int E, int nblk, int b,
+                                                     unsigned int *s_part, int &nbad, Between &&between) {
     const int tid = threadIdx.x;
-    constexpr int kBatch = 16;
-    for (int t0 = 0; t0 < nblk; t0 += kBatch) {
-        int ev[kBatch];
+    unsigned int *__restrict__ part = s_part + (tid & ((1 << CL) - 1));
+    const unsigned int uE = static_cast<unsigned>(E);
+    if (N <= 0 || nblk <= 0) {
+        between();
+        return;
+    }
+    if ((reinterpret_cast<uintptr_t>(idx) & 15u) == 0) {
+        constexpr int kGroup = 4 * kLayoutThreads;  // entries per round of 16-byte loads
+        constexpr int kBatch = 8;
+        for (int g0 = 0; g0 * kGroup < N; g0 += kBatch) {
+            int4 q[kBatch];
 #pragma unroll
-        for (int u = 0; u < kBatch; ++u) {
-            const int t = t0 + u, i = t * kLayoutThreads + tid;
-            ev[u] = (t < nblk && t != b && i < N) ? idx[i] : 0;
-        }
+            for (int u = 0; u < kBatch; ++u) {
+                const int i = (g0 + u) * kGroup + 4 * tid;
+                if (i + 3 < N && i / kLayoutThreads != b) {
+                    q[u] = *reinterpret_cast<const int4 *>(idx + i);
+                } else if (i < N && i / kLayoutThreads != b) {  // the ragged end of the batch
+                    q[u].x = idx[i];
+                    q[u].y = i + 1 < N ? idx[i + 1] : -1;
+                    q[u].z = i + 2 < N ? idx[i + 2] : -1;
+                    q[u].w = -1;
+                    nbad -= i + 4 - N;
+                }
+            }
+            if (g0 == 0) between();
 #pragma unroll
-        for (int u = 0; u < kBatch; ++u) {
-            const int t = t0 + u, i = t * kLayoutThreads + tid;
-            if (t < nblk && t != b && i < N) {
-                const int e = ev[u];
-                if (e >= 0 && e < E) {
-                    atomicAdd(t < b ? &s_before[e] : &s_after[e], 1);
-                } else {
-                    flags |= FLAG_BAD_EXPERT;
-                    ++bad;
+            for (int u = 0; u < kBatch; ++u) {
+                const int i = (g0 + u) * kGroup + 4 * tid, t = i / kLayoutThreads;
+                if (i >= N || t == b) continue;
+                const unsigned int inc = t < b ? 0x10001u : 1u;
+                const int e4[4] = {q[u].x, q[u].y, q[u].z, q[u].w};
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const bool ok = static_cast<unsigned>(e4[j]) < uE;
+                    nbad += ok ? 0 : 1;
+                    atomicAdd(part + ((ok ? e4[j] : E) << CL), inc);
                 }
             }
         }
+    } else {
+        // idx not 16-byte aligned: entry t*1024 + tid of every tile t, 16 loads in flight
+        constexpr int kBatch = 16;
+        for (int t0 = 0; t0 < nblk; t0 += kBatch) {
+            int ev[kBatch];
+#pragma unroll
+            for (int u = 0; u < kBatch; ++u) {
+                const int t = t0 + u, i = t * kLayoutThreads + tid;
+                ev[u] = (t < nblk && t != b && i < N) ? idx[i] : 0;
+            }
+            if (t0 == 0) between();
+#pragma unroll
+            for (int u = 0; u < kBatch; ++u) {
+                const int t = t0 + u, i = t * kLayoutThreads + tid;
+                if (t >= nblk || t == b || i >= N) continue;
+                const bool ok = static_cast<unsigned>(ev[u]) < uE;
+                nbad += ok ? 0 : 1;
+                atomicAdd(part + ((ok ? ev[u] : E) << CL), t < b ? 0x10001u : 1u);
+            }
+        }
     }
+}
+
+// Counts every entry outside tile b into s_part (zeroed).  Entries with an
+// expert outside [0,E) set FLAG_BAD_EXPERT in flags and are added to bad.
+// Redundant work that lets one workgroup per tile know every count without
+// talking to the others.  `between()` runs once, after the first loads are
+// issued and before their counts: the caller's own work there (ranking its
+// own tile) overlaps the load latency.
+//
+// Thread tid reads entries 4*tid + 4096*g (g = 0, 1, ...), four at a time with
+// one 16-byte load when idx is 16-byte aligned, 8 such loads in flight: at 32
+// tiles that is every load the thread makes, issued at once, and the count is
+// then bound by the LDS atomics alone (one-by-one 4-byte loads in two batches
+// of 16 kept the workgroup ~1.5 us longer on MI355X).  Four consecutive
+// entries never straddle a tile, so each load's tile is one test.
+template <typename Between>
+__device__ __forceinline__ void count_other_tiles(const int32_t *__restrict__ idx, int N, int E, int nblk, int b,
+                                                  unsigned int *s_part, int &flags, int &bad, Between &&between) {
+    int nbad = 0;
+    const int cl = other_copies_log2(E);
+    if (cl == 3)
+        count_other_tiles_cl<3>(idx, N, E, nblk, b, s_part, nbad, between);
+    else if (cl == 2)
+        count_other_tiles_cl<2>(idx, N, E, nblk, b, s_part, nbad, between);
+    else
+        count_other_tiles_cl<1>(idx, N, E, nblk, b, s_part, nbad, between);
+    if (nbad) flags |= FLAG_BAD_EXPERT;
+    bad += nbad;
+}
+
+// After count_other_tiles and a workgroup barrier: expert e's packed counter
+// summed over its copies (contiguous: one or two 16-byte LDS reads).  s_part
+// must be 16-byte aligned.
+__device__ __forceinline__ unsigned int other_total(const unsigned int *s_part, int E, int e) {
+    const int cl = other_copies_log2(E);
+    if (cl == 3) {
+        const uint4 x = reinterpret_cast<const uint4 *>(s_part)[2 * e];
+        const uint4 y = reinterpret_cast<const uint4 *>(s_part)[2 * e + 1];
+        return (x.x + x.y) + (x.z + x.w) + (y.x + y.y) + (y.z + y.w);
+    }
+    if (cl == 2) {
+        const uint4 x = reinterpret_cast<const uint4 *>(s_part)[e];
+        return (x.x + x.y) + (x.z + x.w);
+    }
+    const uint2 x = reinterpret_cast<const uint2 *>(s_part)[e];
+    return x.x + x.y;
 }
 
 }  // namespace moe

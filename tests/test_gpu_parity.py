@@ -800,3 +800,45 @@ def test_layout_balanced(moe, case):
     out = moe.moe_combine(desc, lay, dev_bf16(y, DEV), tw_d)
     torch.cuda.synchronize()
     assert_combine_matches(host_bits(out), oracle.combine(y, ref.pos, tw), "balanced combine")
+
+
+# name, S, K, E, R, pad mode, pad rows: entry counts S*K that are not multiples of
+# 4, in the single-workgroup, small-batch, one-launch and two-launch layouts
+IDX_OFFSET = [
+    ("single-N1999", 1999, 1, 32, 4, PAD_NONE, 0),
+    ("small-N4093", 4093, 1, 256, 8, PAD_CAPACITY, 24),
+    ("onepass-N9999", 3333, 3, 256, 8, PAD_NONE, 0),
+    ("onepass-N30002", 15001, 2, 64, 8, PAD_MULTIPLE, 16),
+    ("onepass-N32767", 32767, 1, 128, 4, PAD_NONE, 0),
+    ("multi-N40001", 40001, 1, 96, 6, PAD_NONE, 0),
+]
+
+
+@pytest.mark.parametrize("offset", [0, 1], ids=["aligned", "idx-off-by-4-bytes"])
+@pytest.mark.parametrize("case", IDX_OFFSET, ids=[c[0] for c in IDX_OFFSET])
+def test_layout_idx_alignment(moe, case, offset):
+    """topk_idx carries no alignment requirement: the layouts read it four
+    entries at a time only when it is 16-byte aligned.  Both forms, with a
+    ragged last group of four, against the oracle (plain and balanced)."""
+    name, S, K, E, R, pad_mode, pad_rows = case
+    seed = 7100 + IDX_OFFSET.index(case)
+    rng = np.random.default_rng(seed)
+    p = rng.random(E) ** 2
+    idx = rng.choice(E, size=(S, K), p=p / p.sum()).astype(np.int32)
+    idx.reshape(-1)[rng.integers(0, idx.size, 5)] = E + 3   # a few invalid ids
+    say(f"case idx alignment {name} offset={offset}: S={S} K={K} E={E} R={R} pad={pad_mode}/{pad_rows}")
+    store = torch.zeros(S * K + 4, dtype=torch.int32, device=DEV)
+    view = store[offset:offset + S * K].view(S, K)
+    view.copy_(torch.from_numpy(idx))
+    assert (view.data_ptr() % 16 == 0) == (offset == 0)
+    desc = moe.LayoutDesc(S, K, E, R, pad_mode, pad_rows)
+    lay = moe.moe_layout(desc, view)
+    torch.cuda.synchronize()
+    compare_layout(lay, oracle.layout(idx, E, R, pad_mode, pad_rows), f"{name} layout")
+    lay_b, bal = moe.moe_layout_balanced(moe.LayoutDesc(S, K, E, R), 4, view)
+    torch.cuda.synchronize()
+    ref = oracle.layout_balanced(idx, E, R, 4)
+    for k in ("tokens_per_expert", "tokens_per_rank", "expert_offset", "rank_offset", "pos", "src", "status"):
+        want = getattr(ref, k)
+        assert np.array_equal(getattr(lay_b, k).cpu().numpy().reshape(want.shape), want), f"balanced {k}"
+    assert np.array_equal(bal.seg_offset.cpu().numpy(), ref.seg_offset)
