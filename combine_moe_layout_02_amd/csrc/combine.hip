@@ -15,13 +15,20 @@
 // indices and weights are wave-uniform scalars.  Workgroups are numbered
 // chunk-fastest, so the waves running at one time cover whole source rows
 // rather than one chunk of thousands of rows: on MI355X that DRAM-friendlier
-// order measured about 6% faster than a token-fastest order.
+// order measured about 6% faster than a token-fastest order.  The gathers are
+// non-temporal loads (ordinary loads measured ~14 % slower in the step).
 #include "moe_kernels.h"
 
 namespace moe {
 namespace {
 
 typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// Word 3 of a raw buffer descriptor on gfx950 (32-bit data format, no
+// swizzle, no index stride) and the cache-policy operand bit that sets SC1 on
+// a buffer store (bit 0 is SC0, bit 1 NT).
+constexpr int kBufferRsrcWord3 = 0x00020000;
+constexpr int kCachePolicySc1 = 1 << 4;
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 // two fp32 -> packed bf16 pair, round to nearest even (v_cvt_pk_bf16_f32)
@@ -76,9 +83,15 @@ __global__ __launch_bounds__(kWave) void k_combine(CombineArgs a, int nchunk) {
     u32x4 o;
 #pragma unroll
     for (int i = 0; i < 4; ++i) o[i] = pack_bf16x2(acc[2 * i], acc[2 * i + 1]);
-    // ordinary store for out, non-temporal loads for the gathered rows: the
-    // faster pairing in measurements on MI355X
-    static_cast<u32x4 *>(a.out)[static_cast<size_t>(t) * nvec + v] = o;
+    // The output row is stored with the SC1 cache-policy bit (a buffer store
+    // through a descriptor based at this token's row): the line goes on past
+    // this XCD's L2 instead of staying there dirty among the non-temporal
+    // gathers.  In the prefill step on MI355X this took the kernel from
+    // ~93 to ~89 us; a plain, non-temporal or SC0 store, or NT together with
+    // SC1, measured 92-94 us.
+    const __amdgpu_buffer_rsrc_t out_row = __builtin_amdgcn_make_buffer_rsrc(
+        static_cast<char *>(a.out) + static_cast<size_t>(t) * a.H * 2, 0, a.H * 2, kBufferRsrcWord3);
+    __builtin_amdgcn_raw_buffer_store_b128(o, out_row, v * 16, 0, kCachePolicySc1);
 }
 
 }  // namespace
