@@ -89,9 +89,14 @@ __global__ __launch_bounds__(kWave) void k_combine(CombineArgs a, int nchunk) {
     // gathers.  In the prefill step on MI355X this took the kernel from
     // ~93 to ~89 us; a plain, non-temporal or SC0 store, or NT together with
     // SC1, measured 92-94 us.
+    // The record count and the offset are unsigned 32-bit: 2*H bytes per row
+    // is below 2^32 for any int H.
+    const unsigned int row_bytes = static_cast<unsigned int>(a.H) * 2u;
     const __amdgpu_buffer_rsrc_t out_row = __builtin_amdgcn_make_buffer_rsrc(
-        static_cast<char *>(a.out) + static_cast<size_t>(t) * a.H * 2, 0, a.H * 2, kBufferRsrcWord3);
-    __builtin_amdgcn_raw_buffer_store_b128(o, out_row, v * 16, 0, kCachePolicySc1);
+        static_cast<char *>(a.out) + static_cast<size_t>(t) * row_bytes, 0, static_cast<int>(row_bytes),
+        kBufferRsrcWord3);
+    __builtin_amdgcn_raw_buffer_store_b128(o, out_row, static_cast<int>(static_cast<unsigned int>(v) * 16u), 0,
+                                           kCachePolicySc1);
 }
 
 }  // namespace

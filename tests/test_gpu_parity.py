@@ -132,6 +132,10 @@ EDGE = [
     (_case("onepass-N4097-E128", 4097, 64, 128, 1, 8, PAD_MULTIPLE, 3), False, None, False),
     (_case("small-capacity-overflow", 400, 128, 128, 8, 8, PAD_CAPACITY, 20), True, None, False),
     (_case("small-bad-ids", 200, 64, 96, 4, 4, PAD_MULTIPLE, 16), False, "bad", True),
+    # wide rows: many 1 KiB chunks per token, a ragged last chunk, 128 KiB
+    # output rows (combine stores through a descriptor based at each row)
+    (_case("wide-row-bf16-H65544", 40, 65544, 16, 4, 4), False, None, True),
+    (_case("wide-row-fp8-H32896", 24, 32896, 8, 3, 2, PAD_MULTIPLE, 4), True, None, False),
 ]
 
 
@@ -603,6 +607,9 @@ FUSED = [
     # the one-launch form's token limit (S <= 512) at S*K <= 4096
     ("fused-S512-N4096", 512, 1024, 256, 8, 8, PAD_CAPACITY, 20, True, "uniform"),
     ("fallback-S513-N3591", 513, 1024, 128, 7, 8, PAD_MULTIPLE, 4, False, "uniform"),
+    # rows wider than one workgroup's slice (several chunks per token, ragged last one)
+    ("wide-fp8-H16512", 48, 16512, 32, 4, 4, PAD_CAPACITY, 12, True, "uniform"),
+    ("wide-bf16-H8200", 64, 8200, 16, 2, 2, PAD_NONE, 0, False, "uniform"),
 ]
 
 
