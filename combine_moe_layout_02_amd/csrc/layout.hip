@@ -140,6 +140,7 @@ __global__ __launch_bounds__(kLayoutThreads) void k_layout_fused(LayoutArgs a) {
 // status; every workgroup marks its share of padding rows.  64 workgroups even
 // for a few entries: at fixed capacity a decode batch has ~31,000 padding rows
 // to mark, and fewer workgroups took longer (16: +0.7 us, 1: +24 us).
+constexpr int kPlaceShare = 16;  // threads per expert reading tile histograms in k_layout_place
 constexpr int kSmallMinE = 64;  // with fewer experts the single workgroup measured faster
 constexpr int kSmallThreads = 256;
 constexpr int kSmallBlocks = small::kMaxN / kWave;
@@ -209,6 +210,7 @@ template <int J>
 __global__ __launch_bounds__(kLayoutThreads) void k_layout_place(LayoutArgs a) {
     __shared__ int s_off[kMaxE + 1], s_pex[kMaxE + 1], s_pre[kMaxE];
     __shared__ int2 s_tmp[kLayoutWaves];
+    __shared__ int2 s_part[kLayoutThreads];  // [P][E] partial (before b, all) sums
     __shared__ int s_flags;
     const int tid = threadIdx.x, b = blockIdx.x;
     // this tile's expert ids and tile ranks, loaded first: nothing below
@@ -221,31 +223,46 @@ __global__ __launch_bounds__(kLayoutThreads) void k_layout_place(LayoutArgs a) {
         rank_in[j] = i < a.N ? a.pos[i] : -1;
     }
     if (tid == 0) s_flags = 0;
-    int cnt = 0;
-    if (tid < a.E) {
-        // expert tid: entries in tiles before b (in tile order), and in all
-        // tiles.  Up to 32 histogram loads in flight at once: the histograms
-        // were written by other XCDs, so each round trip misses this L2.
-        constexpr int kBatch = 32;
-        int pre = 0;
-        for (int t = 0; t < a.nblk; t += kBatch) {
+    // Per expert, the entries in the tiles before b and in all tiles, from the
+    // per-tile histograms.  P threads share an expert (thread tid: expert
+    // tid % E, tiles tid / E, tid / E + P, ...) and meet in LDS: the
+    // histograms were written by other XCDs, so every load misses this L2,
+    // and one thread per expert took two rounds of 32 such loads at 48 tiles.
+    const int P = min(kLayoutThreads / a.E, kPlaceShare);
+    if (tid < P * a.E) {
+        const int e = tid % a.E, q = tid / a.E;
+        int2 part = make_int2(0, 0);
+        constexpr int kBatch = 16;
+        for (int t0 = q; t0 < a.nblk; t0 += kBatch * P) {
             int c[kBatch];
 #pragma unroll
-            for (int u = 0; u < kBatch; ++u)
-                c[u] = t + u < a.nblk ? a.blk_hist[static_cast<size_t>(t + u) * a.E + tid] : 0;
+            for (int u = 0; u < kBatch; ++u) {
+                const int t = t0 + u * P;
+                c[u] = t < a.nblk ? a.blk_hist[static_cast<size_t>(t) * a.E + e] : 0;
+            }
 #pragma unroll
             for (int u = 0; u < kBatch; ++u) {
-                pre += (t + u < b) ? c[u] : 0;
-                cnt += c[u];
+                part.x += (t0 + u * P < b) ? c[u] : 0;
+                part.y += c[u];
             }
         }
-        s_pre[tid] = pre;
+        s_part[q * a.E + e] = part;
     }
     int flags = 0;
     if (b == 0)
         for (int t = tid; t < a.nblk; t += kLayoutThreads) flags |= a.blk_flags[t];
     __syncthreads();
-    flags |= finish_counts(a, cnt, s_off, s_pex, s_tmp, b == 0, b, a.nblk);
+    int cnt = 0;
+    if (tid < a.E) {
+        int pre = 0;
+        for (int q = 0; q < P; ++q) {
+            const int2 v = s_part[q * a.E + tid];
+            pre += v.x;
+            cnt += v.y;
+        }
+        s_pre[tid] = pre;
+    }
+    flags |= finish_counts(a, cnt, s_off, s_pex, s_tmp, b == 0, b, a.nblk);  // synchronises the workgroup
     // tile b's entries: tile rank -> row
 #pragma unroll
     for (int j = 0; j < J; ++j) {
