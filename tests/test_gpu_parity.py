@@ -818,6 +818,9 @@ IDX_OFFSET = [
     ("onepass-N30002", 15001, 2, 64, 8, PAD_MULTIPLE, 16),
     ("onepass-N32767", 32767, 1, 128, 4, PAD_NONE, 0),
     ("multi-N40001", 40001, 1, 96, 6, PAD_NONE, 0),
+    # the count's 4- and 2-copy counters (E in (256, 512] and (512, 1024])
+    ("onepass-N20001-E264", 20001, 1, 264, 8, PAD_CAPACITY, 70),
+    ("onepass-N9003-E1000", 3001, 3, 1000, 8, PAD_MULTIPLE, 2),
 ]
 
 
