@@ -852,3 +852,38 @@ def test_layout_idx_alignment(moe, case, offset):
         want = getattr(ref, k)
         assert np.array_equal(getattr(lay_b, k).cpu().numpy().reshape(want.shape), want), f"balanced {k}"
     assert np.array_equal(bal.seg_offset.cpu().numpy(), ref.seg_offset)
+
+
+def test_layout_random_sweep(moe):
+    """2,000 seeded random layouts, plain and balanced, every output against the
+    oracle: all layout variants (small, single, one-launch, two-launch), every
+    pad mode, skewed and uniform routing, invalid ids, and topk_idx at every
+    4-byte offset inside a 16-byte line."""
+    rng = np.random.default_rng(20261203)
+    for n in range(2000):
+        R = int(rng.choice([1, 2, 4, 8, 16]))
+        E = R * int(rng.integers(1, 1024 // R + 1))
+        K = int(rng.integers(1, 17))
+        N = int(rng.choice([rng.integers(1, 4097), rng.integers(4097, 32769), rng.integers(32769, 70000)]))
+        S = max(1, N // K)
+        pad_mode = int(rng.integers(0, 3))
+        pad_rows = 0 if pad_mode == PAD_NONE else int(rng.integers(1, 200))
+        p = rng.random(E) ** float(rng.choice([0.0, 1.0, 4.0]))
+        idx = rng.choice(E, size=(S, K), p=p / p.sum()).astype(np.int32)
+        if rng.random() < 0.3:
+            idx.reshape(-1)[rng.integers(0, idx.size, 7)] = int(rng.choice([-1, E, E + 5]))
+        offset = int(rng.integers(0, 4))
+        B = int(rng.integers(0, min(64, 512 // R) + 1))
+        case = f"sweep {n}: S={S} K={K} E={E} R={R} pad={pad_mode}/{pad_rows} offset={offset} B={B}"
+        store = torch.zeros(S * K + 4, dtype=torch.int32, device=DEV)
+        view = store[offset:offset + S * K].view(S, K)
+        view.copy_(torch.from_numpy(idx))
+        lay = moe.moe_layout(moe.LayoutDesc(S, K, E, R, pad_mode, pad_rows), view)
+        torch.cuda.synchronize()
+        compare_layout(lay, oracle.layout(idx, E, R, pad_mode, pad_rows), case)
+        lay_b, _ = moe.moe_layout_balanced(moe.LayoutDesc(S, K, E, R), B, view)
+        torch.cuda.synchronize()
+        ref = oracle.layout_balanced(idx, E, R, B)
+        for k in ("tokens_per_expert", "tokens_per_rank", "expert_offset", "rank_offset", "pos", "src", "status"):
+            want = getattr(ref, k)
+            assert np.array_equal(getattr(lay_b, k).cpu().numpy().reshape(want.shape), want), f"{case}: balanced {k}"
