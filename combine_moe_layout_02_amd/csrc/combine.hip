@@ -11,7 +11,8 @@
 //                      starting at +0.0, then + shared[t,c] ).
 // One wavefront per 512-channel (1 KiB) chunk of a token row.  A lane owns 8
 // channels: it issues all K 16-byte gathers before the first fma (K loads in
-// flight), keeps 8 fp32 accumulators, and writes one 16-byte store.  The K row
+// flight), keeps 8 fp32 accumulators, and writes one 16-byte store (with the
+// SC1 cache-policy bit; see the end of the kernel).  The K row
 // indices and weights are wave-uniform scalars.  Workgroups are numbered
 // chunk-fastest, so the waves running at one time cover whole source rows
 // rather than one chunk of thousands of rows: on MI355X that DRAM-friendlier
@@ -23,13 +24,13 @@ namespace moe {
 namespace {
 
 typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 // Word 3 of a raw buffer descriptor on gfx950 (32-bit data format, no
 // swizzle, no index stride) and the cache-policy operand bit that sets SC1 on
 // a buffer store (bit 0 is SC0, bit 1 NT).
 constexpr int kBufferRsrcWord3 = 0x00020000;
 constexpr int kCachePolicySc1 = 1 << 4;
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 // two fp32 -> packed bf16 pair, round to nearest even (v_cvt_pk_bf16_f32)
 __device__ __forceinline__ unsigned int pack_bf16x2(float lo, float hi) {

@@ -43,7 +43,7 @@ template <int K>
 __device__ __forceinline__ void write_recv_w(const DispatchArgs &a, const int (&p)[K], float w) {
     int row = -1;
 #pragma unroll
-    for (int k = 0; k < K; ++k) row = threadIdx.x == k ? p[k] : row;
+    for (int k = 0; k < K; ++k) row = static_cast<int>(threadIdx.x) == k ? p[k] : row;
     if (row >= 0) a.recv_w[row] = w;
 }
 
