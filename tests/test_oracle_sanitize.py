@@ -14,7 +14,7 @@ import pytest
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
-DRIVER = os.path.join(HERE, "oracle_sanitize_main.c")
+MAIN_SRC = os.path.join(HERE, "oracle_sanitize_main.c")
 ORACLE = os.path.join(ROOT, "oracle", "moe_oracle.c")
 
 pytestmark = pytest.mark.skipif(shutil.which("gcc") is None, reason="gcc not found")
@@ -25,7 +25,7 @@ ENV = dict(os.environ, ASAN_OPTIONS="detect_leaks=1", UBSAN_OPTIONS="print_stack
 
 
 def _build_and_run(oracle_src, exe):
-    r = subprocess.run(["gcc", *FLAGS, DRIVER, oracle_src, "-lm", "-o", str(exe)], capture_output=True, text=True)
+    r = subprocess.run(["gcc", *FLAGS, MAIN_SRC, oracle_src, "-lm", "-o", str(exe)], capture_output=True, text=True)
     assert r.returncode == 0, r.stderr
     return subprocess.run([str(exe)], capture_output=True, text=True, env=ENV, timeout=300)
 
