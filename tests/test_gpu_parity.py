@@ -268,7 +268,8 @@ def test_fp8_converter_sweep(moe):
 def test_combine_rounding_order_pins(moe):
     """Hand-worked cases where only an fp32 fma chain in ascending k gives the
     right bf16 bit (the same cases pin the oracle): 1+2^-8 then
-    0x1.fc07f2p-25 * (1+2^-7) -> 0x3F81; 1+2^-8, 3*2^-26, 3*2^-26 -> 0x3F80."""
+    0x1.fc07f2p-25 * (1+2^-7) -> 0x3F81; 1+2^-8, 3*2^-26, 3*2^-26 -> 0x3F80;
+    and one where only adding the shared output after the chain does."""
     H = 8
     one, one_p = 0x3F80, 0x3F81
     for ws, ys, want in (([1 + 2 ** -8, float.fromhex("0x1.fc07f2p-25")], [one, one_p], 0x3F81),
@@ -281,6 +282,15 @@ def test_combine_rounding_order_pins(moe):
         y = np.repeat(np.array(ys, np.uint16)[:, None], H, axis=1)
         out = moe.moe_combine(desc, lay, dev_bf16(y, DEV), torch.tensor([ws], dtype=torch.float32, device=DEV))
         assert host_bits(out).tolist() == [[want] * H]
+    # the shared output is added after the routed chain: 2^-8+3*2^-26 and
+    # 3*2^-26 (y = 1.0) plus shared 1.0 -> 0x3F81 (shared first would give 0x3F80)
+    say("case order-pin shared-last")
+    desc = moe.LayoutDesc(1, 2, 2, 1)
+    lay = moe.moe_layout(desc, torch.arange(2, dtype=torch.int32, device=DEV).reshape(1, 2))
+    y = np.full((2, H), one, np.uint16)
+    ws = torch.tensor([[2 ** -8 + 3 * 2 ** -26, 3 * 2 ** -26]], dtype=torch.float32, device=DEV)
+    out = moe.moe_combine(desc, lay, dev_bf16(y, DEV), ws, shared_out=dev_bf16(np.full((1, H), one, np.uint16), DEV))
+    assert host_bits(out).tolist() == [[0x3F81] * H]
 
 
 def test_round_trip_on_gpu(moe):

@@ -11,6 +11,7 @@ writes to the final expert-grouped slot with static shapes (MoonEP article,
 section 2); token_padding (MoonEP article, basic usage).
 """
 import itertools
+from fractions import Fraction
 
 import numpy as np
 import pytest
@@ -368,6 +369,132 @@ def test_fp8_zero_block_and_sign_symmetry():
     assert np.all(ncodes[:128] == 0)   # all-zero block (now -0.0) still gives 0x00
 
 
+# Exact rational arithmetic: the correctly rounded fp32 result of an operation
+# is the fp32 value nearest its exact value (ties to the even significand).
+# Written from the IEEE 754 definition, independent of any float hardware.
+
+
+def f32_nearest(r: Fraction) -> Fraction:
+    """Nearest fp32 value to the exact rational r (normal range), ties to even."""
+    if r == 0:
+        return Fraction(0)
+    sign = -1 if r < 0 else 1
+    a = abs(r)
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    if Fraction(2) ** e > a:
+        e -= 1
+    assert Fraction(2) ** e <= a < Fraction(2) ** (e + 1) and -126 <= e <= 127
+    ulp = Fraction(2) ** (e - 23)
+    n, rem = divmod(a, ulp)
+    if rem * 2 > ulp or (rem * 2 == ulp and n % 2 == 1):
+        n += 1
+    return sign * n * ulp
+
+
+def e4m3_nearest_exact(r: Fraction) -> int:
+    """E4M3FN code of the exact rational r: the nearest finite code value, ties
+    to the even mantissa, saturating at +-448, the sign of r kept."""
+    sign = 0x80 if r < 0 else 0x00
+    a = abs(r)
+    best = None
+    for c in range(0x7F):                       # 0x00..0x7E: every finite magnitude
+        e, m = c >> 3, c & 7
+        v = Fraction(m, 512) if e == 0 else Fraction(8 + m, 8) * Fraction(2) ** (e - 7)
+        d = abs(v - a)
+        if best is None or d < best[0] or (d == best[0] and c % 2 == 0):
+            best = (d, c)
+    return sign | best[1]
+
+
+def _f32_exact(v) -> Fraction:
+    return Fraction(float(np.float32(v)))
+
+
+def test_fp8_hand_block_scale_and_quotient_rounding():
+    """One block where the readings of the quantiser give different bits.
+
+    amax = 1.53125 (bf16 0x3FC4) = 49/32, so amax/448 = 7/2048 exactly; amax
+    times a rounded 1/448 lands one fp32 step above it.  The element
+    x = 0.0247802734375 (bf16 0x3CCB) divided by the exact scale gives 7.25,
+    exactly halfway between the E4M3 values 7.0 and 7.5, so the tie goes to
+    the even mantissa: 7.0, code 0x4E.  x times a rounded 448/amax, or times a
+    rounded 1/scale, gives 7.25 + 2^-21, past the midpoint: 7.5, code 0x4F.
+    Expected bits come from exact rational arithmetic only; the other readings
+    are asserted to differ so the case stays discriminating."""
+    amax_bits, x_bits = 0x3FC4, 0x3CCB
+    amax = Fraction(1.53125)
+    x = Fraction(0.0247802734375)
+    assert _f32_exact((np.uint32(amax_bits) << 16).view(np.float32)) == amax
+    assert _f32_exact((np.uint32(x_bits) << 16).view(np.float32)) == x
+    scale = f32_nearest(amax / 448)
+    q = f32_nearest(x / scale)
+    code_x = e4m3_nearest_exact(q)
+    # the alternative readings, each step rounded to fp32
+    scale_recip = f32_nearest(amax * f32_nearest(Fraction(1, 448)))
+    q_mul448 = f32_nearest(x * f32_nearest(448 / amax))
+    q_recip = f32_nearest(x * f32_nearest(1 / scale))
+    assert scale_recip != scale
+    assert e4m3_nearest_exact(q_mul448) != code_x and e4m3_nearest_exact(q_recip) != code_x
+    assert scale == Fraction(7, 2048) and q == Fraction(29, 4)
+    assert code_x == 0x4E                       # 7.0 = 2^2 * (1 + 6/8)
+
+    row = np.zeros(256, np.uint16)
+    row[3], row[40], row[77] = amax_bits, x_bits, x_bits | 0x8000
+    row[128 + 5] = 0xBFC4                       # second block: amax from a negative value
+    row[128 + 6] = x_bits
+    codes, scales = oracle.quantize_row_fp8(row)
+    assert Fraction(float(scales[0])) == scale and Fraction(float(scales[1])) == scale
+    assert codes[3] == 0x7E and codes[128 + 5] == 0xFE
+    assert codes[40] == code_x and codes[77] == (code_x | 0x80) and codes[128 + 6] == code_x
+    others = np.ones(256, bool)
+    others[[3, 40, 77, 128 + 5, 128 + 6]] = False
+    assert np.all(codes[others] == 0x00)
+
+
+def e4m3_nearest_vec(v: np.ndarray) -> np.ndarray:
+    """Vectorised exhaustive search: for each value, the nearest of the 127
+    finite non-negative code magnitudes to |v| (ties to the even mantissa), with
+    v's sign bit set on the code.  Distances in float64 are exact here
+    (|v| <= 2^9, every code and every fp32 input is a short dyadic rational)."""
+    tab = e4m3_table()[:0x7F]
+    v = np.asarray(v, np.float32)
+    a = np.abs(v).astype(np.float64)
+    out = np.empty(a.shape, np.uint8)
+    flat_a, flat_o = a.reshape(-1), out.reshape(-1)
+    for i in range(0, flat_a.size, 1 << 15):
+        d = np.abs(tab[None, :] - flat_a[i:i + (1 << 15), None])
+        best = d.min(axis=1, keepdims=True)
+        hit = d == best
+        n_hit = hit.sum(axis=1)
+        first = hit.argmax(axis=1)
+        # a tie is between two neighbouring codes: keep the even one
+        pick = np.where((n_hit > 1) & (first % 2 == 1), first + 1, first)
+        flat_o[i:i + (1 << 15)] = pick
+    return out | np.where(np.signbit(v), 0x80, 0x00).astype(np.uint8)
+
+
+@pytest.mark.parametrize("name,tokens", [("decode", 128), ("prefill", 512)])
+def test_fp8_codes_and_scales_vs_numpy_division(name, tokens):
+    """Every block of the decode batch and of 512 prefill tokens, recomputed
+    outside the oracle: the scale is numpy's IEEE fp32 quotient amax / 448, each
+    code the exhaustive nearest-code search applied to numpy's fp32 quotient
+    x / scale.  Codes and scale bits must be identical."""
+    cfg = CONFIGS[name]
+    hid = make_workload(cfg).hidden[:tokens]
+    x = (hid.astype(np.uint32) << 16).view(np.float32).reshape(tokens, -1, 128)
+    amax = np.abs(x).max(axis=2)
+    assert np.all(amax > 0)
+    scale = amax / np.float32(448.0)
+    assert scale.dtype == np.float32
+    q = x / scale[:, :, None]
+    assert q.dtype == np.float32
+    want_codes = e4m3_nearest_vec(q).reshape(tokens, -1)
+    for t in range(tokens):
+        codes, scales = oracle.quantize_row_fp8(hid[t])
+        assert np.array_equal(scales.view(np.uint32), scale[t].view(np.uint32)), t
+        assert np.array_equal(codes, want_codes[t]), t
+
+
 # ---------------------------------------------------------------------------
 # combine
 # ---------------------------------------------------------------------------
@@ -393,6 +520,31 @@ def test_combine_fma_chain_order_pins():
     pos3 = np.array([[0, 2, 2]], np.int32)
     w3 = np.array([[1 + 2 ** -8, 3 * 2 ** -26, 3 * 2 ** -26]], np.float32)
     assert oracle.combine(y, pos3, w3).tolist() == [[0x3F80]]
+
+
+def test_combine_shared_added_after_chain():
+    """Shared output added after the routed fma chain, not used as its start.
+
+    Terms w0*y0 = 2^-8 + 3*2^-26 and w1*y1 = 3*2^-26 (y = 1.0), shared = 1.0.
+    Routed chain first: the two small parts meet at the scale of 2^-8 and sum
+    exactly to 2^-8 + 6*2^-26; adding 1.0 then leaves 0.75 of an fp32 step at 1
+    past 1 + 2^-8, which rounds up to 1 + 2^-8 + 2^-23, above the bf16 midpoint:
+    bf16 1 + 2^-7 = 0x3F81.  Starting the chain from the shared 1.0 instead,
+    each small part is 0.375 of a step and is absorbed, leaving exactly the
+    midpoint 1 + 2^-8, which ties to the even bf16 1.0 = 0x3F80."""
+    y = np.array([[0x3F80], [0x3F80]], np.uint16)
+    pos = np.array([[0, 1]], np.int32)
+    w = np.array([[2 ** -8 + 3 * 2 ** -26, 3 * 2 ** -26]], np.float32)
+    assert float(w[0, 0]) == 2 ** -8 + 3 * 2 ** -26 and float(w[0, 1]) == 3 * 2 ** -26
+    shared = np.array([[0x3F80]], np.uint16)
+    # the two orders, every step rounded to fp32 in exact arithmetic
+    t0, t1, one = Fraction(float(w[0, 0])), Fraction(float(w[0, 1])), Fraction(1)
+    last = f32_nearest(f32_nearest(f32_nearest(t0) + t1) + one)
+    first = f32_nearest(f32_nearest(one + t0) + t1)
+    assert last == 1 + Fraction(1, 256) + Fraction(1, 2 ** 23) and first == 1 + Fraction(1, 256)
+    assert oracle.combine(y, pos, w, shared).tolist() == [[0x3F81]]
+    # without the shared output the chain alone is 2^-8 + 6*2^-26 -> bf16 2^-8
+    assert oracle.combine(y, pos, w).tolist() == [[0x3B80]]
 
 
 @pytest.mark.parametrize("name", ["tiny", "dsmoe16b"])
