@@ -53,9 +53,12 @@ __global__ __launch_bounds__(kWave) void k_combine(CombineArgs a, int nchunk) {
 #pragma unroll
     for (int k = 0; k < K; ++k) {
         p[k] = pos[k];
-        // an entry that was not placed reads row 0 and is then ignored
-        const size_t row = p[k] >= 0 ? static_cast<size_t>(p[k]) : 0;
-        r[k] = __builtin_nontemporal_load(y + row * nvec + v);
+        // p[k] is the same for the whole wave, so this is a scalar branch; an
+        // entry that was not placed reads nothing
+        if (p[k] >= 0)
+            r[k] = __builtin_nontemporal_load(y + static_cast<size_t>(p[k]) * nvec + v);
+        else
+            r[k] = u32x4{0u, 0u, 0u, 0u};
     }
     float acc[8];
 #pragma unroll

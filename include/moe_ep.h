@@ -178,7 +178,7 @@ moe_status moe_layout_dispatch(const moe_layout_desc *desc, const int32_t *topk_
  *   w           [S,K] fp32 in token order, or NULL for weight 1.
  *   shared_out  [S,H] bf16 or NULL (then nothing is added).
  *   out         [S,H] bf16, 16-byte aligned.
- * Entries with pos = -1 are skipped. */
+ * Entries with pos = -1 are skipped: their expert_out row is not read. */
 moe_status moe_combine(const moe_layout_desc *desc, const moe_layout_bufs *layout,
                        const void *expert_out, int32_t H, const float *w,
                        const void *shared_out, void *out, void *stream);

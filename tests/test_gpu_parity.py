@@ -698,35 +698,47 @@ def test_layout_dispatch(moe, case):
 
 
 def test_cu_limited_stream(moe):
-    """Layout, dispatch and combine on a stream limited to 32 CUs give the same
-    bits as on the default stream."""
+    """Layout, FP8 dispatch and combine on CU-limited streams (the first 16 and
+    32 CUs, and the upper half of the chip as a placed range), each checked
+    against the oracle: layout and FP8 codes and scales bit for bit, combine of
+    seeded random expert outputs within one bf16 ulp."""
     cfg = CONFIGS["prefill"]
     w = make_workload(cfg)
-    say("case cu-limited stream prefill")
+    say("case cu-limited stream prefill: oracle")
+    ref = oracle.layout(w.topk_idx, cfg.E, cfg.R)
+    rows = len(ref.src)
+    valid = ref.src >= 0
+    rc, rs, rw = oracle.dispatch_fp8(w.hidden, ref.pos, rows, w.topk_w)
+    y = random_expert_out_bits(w.seed, rows, cfg.H, row_mask=valid, poison=POISON_BF16)
+    out_ref = oracle.combine(y, ref.pos, w.topk_w)
     buf = moe.Buffer(cfg.S, cfg.H, cfg.K, cfg.E, cfg.R, fp8=True, device=DEV)
+    assert buf.rows == rows
     idx = torch.from_numpy(w.topk_idx).to(DEV)
     hid = dev_bf16(w.hidden, DEV)
     tw = torch.from_numpy(w.topk_w).to(DEV)
-    y = torch.randn((buf.rows, cfg.H), device=DEV).to(torch.bfloat16)
-    torch.cuda.synchronize()
-
-    def run():
-        buf.layout_call(idx)
-        buf.dispatch_call(hid, idx, tw)
-        buf.combine_call(y, tw)
-        return [t.clone() for t in (buf.layout.pos, buf.layout.src, buf.recv, buf.recv_scales, buf.out)]
-
-    want = run()
-    torch.cuda.synchronize()
+    y_d = dev_bf16(y, DEV)
     n_cu = torch.cuda.get_device_properties(0).multi_processor_count
-    # the first 32 CUs, and the upper half of the chip (a placed range)
-    for first, count in ((0, 32), (n_cu // 2, n_cu // 2)):
+    for first, count in ((0, 16), (0, 32), (n_cu // 2, n_cu // 2)):
+        say(f"case cu-limited stream prefill: CUs [{first}, {first + count})")
+        for lt in (buf.layout.pos, buf.layout.src, buf.layout.tokens_per_expert, buf.layout.expert_offset):
+            lt.fill_(-7)
+        buf.recv.fill_(POISON_U8)
+        buf.recv_scales.fill_(float("nan"))
+        buf.recv_w.fill_(float("nan"))
+        buf.out.view(torch.int16).fill_(POISON_BF16)
+        torch.cuda.synchronize()
         with moe.CULimitedStream(count, DEV, first_cu=first) as cs:
             with torch.cuda.stream(cs.stream):
-                got = run()
+                buf.layout_call(idx)
+                buf.dispatch_call(hid, idx, tw)
+                buf.combine_call(y_d, tw)
             torch.cuda.synchronize()
-        for a, b in zip(got, want):
-            assert torch.equal(a, b)
+        compare_layout(buf.layout, ref, f"layout on {count} CUs")
+        got_c, got_s = buf.recv.cpu().numpy(), buf.recv_scales.cpu().numpy()
+        assert np.array_equal(got_c[valid], rc[valid]), f"fp8 codes on {count} CUs"
+        assert np.array_equal(got_s[valid].view(np.uint32), rs[valid].view(np.uint32)), f"fp8 scales on {count} CUs"
+        assert np.array_equal(buf.recv_w.cpu().numpy()[valid].view(np.uint32), rw[valid].view(np.uint32))
+        assert_combine_matches(host_bits(buf.out), out_ref, f"combine on {count} CUs")
     # ranges the XCD rule refuses
     handle = ctypes.c_void_p()
     lib = moe.lib()
