@@ -11,7 +11,8 @@ Timing: W untimed warm-up steps, then K timed steps bracketed by
 torch.cuda.synchronize(); HIP events on the launch stream around every call
 give per-kernel averages.  A percentile pass adds p10 / median / p90 per call
 over 100 iterations (1000 for the decode call), back to back ("warm") and
-after overwriting 512 MiB, twice the Infinity Cache ("cold").  Bytes are the
+after a read-only pass over 512 MiB, twice the Infinity Cache, which leaves
+no dirty lines behind ("cold").  Bytes are the
 algorithmic bytes the path must move (padding rows excluded), GB = 1e9.
 Beside the prefill batch the same-shape skewed batch (bf16 dispatch, segments
 padded to 128 rows) is timed too.
@@ -20,6 +21,7 @@ padded to 128 rows) is timed too.
   --config NAME      tiny | prefill | decode | skew | dsmoe16b
   --calib-copy       run only a plain device copy of known size (for scaling
                      rocprofv3 FETCH_SIZE / WRITE_SIZE counters)
+  --ceilings         run only the pattern-ceiling kernels (libmoe_ceilings.so)
   --no-cpu-baseline  skip timing the CPU oracle
   --no-decode        skip the decode, balanced-layout and skewed-batch numbers
   --no-percentiles   skip the percentile pass and the streaming reference
@@ -192,59 +194,100 @@ def time_steps(run, steps: int, warmup: int):
     return dict(layout_ms=lay, dispatch_ms=dis, combine_ms=com, step_ms=step_ms, wall_s=wall)
 
 
-def call_percentiles(calls, names, iters: int, flush_bytes: int = 0):
+class CacheFlush:
+    """Evicts the caches between timed iterations without leaving dirty lines.
+
+    A buffer of `nbytes` (twice the 256 MB Infinity Cache for 512 MiB) is
+    written once and synchronised at construction; each flush() then only
+    READS it (a sum into a small result), so the lines it brings in are clean
+    and the write-back of whatever the previous iteration left dirty happens
+    inside the flush, not inside the timed kernels after it."""
+
+    def __init__(self, nbytes: int, dev="cuda"):
+        import torch
+        self.buf = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
+        self.acc = torch.empty((), dtype=torch.float32, device=dev)
+        torch.cuda.synchronize()
+
+    def flush(self):
+        import torch
+        torch.sum(self.buf, dim=0, out=self.acc)
+
+
+def call_percentiles(calls, names, iters: int, flush: "CacheFlush | None" = None, pairs=()):
     """p10 / median / p90 (µs) of each call over `iters` iterations, HIP events
-    on the launch stream around every call.  With flush_bytes, every iteration
-    first overwrites a scratch buffer of that size (twice the 256 MB
-    Infinity Cache for 512 MiB) outside the event pairs: cold-cache timing."""
+    on the launch stream around every call.  With `flush`, every iteration
+    first evicts the caches with a read-only pass (outside the event pairs):
+    cold-cache timing.  `pairs` names tuples of calls whose per-iteration sum
+    is reported too (e.g. dispatch + combine)."""
     import numpy as np
     import torch
-    scratch = torch.empty(flush_bytes, dtype=torch.uint8, device="cuda") if flush_bytes else None
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)] for _ in range(iters)]
     for i in range(iters):
-        if scratch is not None:
-            scratch.fill_(i & 0xFF)
+        if flush is not None:
+            flush.flush()
         ev[i][0].record()
         for j, call in enumerate(calls):
             call()
             ev[i][j + 1].record()
     torch.cuda.synchronize()
-    out = {}
-    for j, name in enumerate(names):
-        us = np.array([ev[i][j].elapsed_time(ev[i][j + 1]) * 1e3 for i in range(iters)])
-        out[name] = [round(float(x), 2) for x in np.percentile(us, [10, 50, 90])]
-    del scratch
+    per = {name: np.array([ev[i][j].elapsed_time(ev[i][j + 1]) * 1e3 for i in range(iters)])
+           for j, name in enumerate(names)}
+    out = {name: [round(float(x), 2) for x in np.percentile(us, [10, 50, 90])] for name, us in per.items()}
+    for group in pairs:
+        us = sum(per[n] for n in group)
+        out["+".join(group)] = [round(float(x), 2) for x in np.percentile(us, [10, 50, 90])]
     return out
 
 
-def percentile_numbers(run, drun, iters: int = 100, decode_iters: int = 1000, trun=None):
+def percentile_numbers(run, drun, iters: int = 100, decode_iters: int = 1000, trun=None, srun=None):
     """Per-call p10 / median / p90 of the step's kernels, warm (back to back)
-    and cold (after a 512 MiB overwrite), at the batch shape, at decode and
-    for the tiny batch (cache-resident: no roofline claim)."""
+    and cold (after a read-only 512 MiB eviction pass), at the batch shape, at
+    decode, for the tiny batch (cache-resident: no roofline claim) and for the
+    same-shape skewed batch."""
+    flush = CacheFlush(512 << 20)
     big = {"calls": ["layout", "dispatch", "combine"], "iters": iters}
     calls = (run.layout_call, run.dispatch_call, run.combine_call)
-    big["warm_us"] = call_percentiles(calls, big["calls"], iters)
-    big["cold_us"] = call_percentiles(calls, big["calls"], iters, 512 << 20)
-    res = {"unit": "us [p10, p50, p90]", "batch": big}
+    pairs = (("dispatch", "combine"),)
+    big["warm_us"] = call_percentiles(calls, big["calls"], iters, pairs=pairs)
+    big["cold_us"] = call_percentiles(calls, big["calls"], iters, flush, pairs=pairs)
+    res = {"unit": "us [p10, p50, p90]", "cold_flush": "read-only sum over 512 MiB written once beforehand",
+           "batch": big}
+    if srun is not None:
+        sk = {"calls": big["calls"], "iters": iters}
+        scalls = (srun.layout_call, srun.dispatch_call, srun.combine_call)
+        sk["warm_us"] = call_percentiles(scalls, sk["calls"], iters, pairs=pairs)
+        sk["cold_us"] = call_percentiles(scalls, sk["calls"], iters, flush, pairs=pairs)
+        res["skew"] = sk
     if drun is not None:
         dec = {"calls": ["layout_dispatch", "combine"], "iters": decode_iters}
         dcalls = (drun.layout_dispatch_call, drun.combine_call)
         dec["warm_us"] = call_percentiles(dcalls, dec["calls"], decode_iters)
-        dec["cold_us"] = call_percentiles(dcalls, dec["calls"], decode_iters, 512 << 20)
+        dec["cold_us"] = call_percentiles(dcalls, dec["calls"], decode_iters, flush)
         res["decode"] = dec
     if trun is not None:
         tiny = {"calls": big["calls"], "iters": decode_iters}
         tcalls = (trun.layout_call, trun.dispatch_call, trun.combine_call)
         tiny["warm_us"] = call_percentiles(tcalls, tiny["calls"], decode_iters)
-        tiny["cold_us"] = call_percentiles(tcalls, tiny["calls"], decode_iters, 512 << 20)
+        tiny["cold_us"] = call_percentiles(tcalls, tiny["calls"], decode_iters, flush)
         res["tiny"] = tiny
+    del flush
     return res
 
 
-def shape_numbers(moe, cfg, dev, steps: int = 30, warmup: int = 5):
+def cold_dc(pct_entry, nbytes: int) -> dict:
+    """Dispatch + combine GB/s and fraction of peak from the median of the
+    per-iteration dispatch + combine time after the read-only flush."""
+    us = pct_entry["cold_us"]["dispatch+combine"][1]
+    gbps = nbytes / (us * 1e-6) / 1e9
+    return {"cold_dispatch_plus_combine_us_median": us, "cold_dispatch_plus_combine_gbps": round(gbps, 1),
+            "cold_dispatch_plus_combine_frac_of_peak": round(gbps / HBM_PEAK_GBPS, 4)}
+
+
+def shape_numbers(moe, cfg, dev, steps: int = 30, warmup: int = 5, run=None):
     """Dispatch + combine GB/s and % of peak of another workload (the skewed
     batch has the metric's shape with bf16 dispatch and padding)."""
-    r = Run(moe, cfg, dev)
+    r = run if run is not None else Run(moe, cfg, dev)
     _, db, cb = r.bytes()
     t = time_steps(r, steps, warmup)
     dc = (db + cb) / ((t["dispatch_ms"] + t["combine_ms"]) * 1e-3) / 1e9
@@ -253,7 +296,6 @@ def shape_numbers(moe, cfg, dev, steps: int = 30, warmup: int = 5):
            "layout_us": round(t["layout_ms"] * 1e3, 2), "dispatch_plus_combine_gbps": round(dc, 1),
            "dispatch_plus_combine_frac_of_peak": round(dc / HBM_PEAK_GBPS, 4),
            "bytes": {"dispatch": db, "combine": cb}}
-    del r
     return out
 
 
@@ -425,6 +467,180 @@ def balanced_numbers(moe, cfg, dev, slots: int = 16, iters: int = 200):
             "replica_slots_used": used, "unbalanced_flag": bool(status & 4)}
 
 
+# ---------------------------------------------------------------------------
+# pattern ceilings (libmoe_ceilings.so: the dispatch / combine byte patterns
+# with no arithmetic)
+# ---------------------------------------------------------------------------
+
+LOAD_KINDS = {"plain": 0, "nt": 1}
+STORE_KINDS = {"plain": 0, "nt": 1, "sc1": 2}
+
+
+def ceiling_lib():
+    import ctypes
+    path = os.path.join(ROOT, "combine_moe_layout_02_amd", "libmoe_ceilings.so")
+    if not os.path.exists(path):
+        raise FileNotFoundError(f"{path} is not built; run __graft_entry__.build()")
+    L = ctypes.CDLL(path)
+    P, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+    L.moe_ceiling_read.argtypes = [P, i64, i32, i32, i32, P, P]
+    L.moe_ceiling_write.argtypes = [P, i64, i32, i32, i32, P]
+    L.moe_ceiling_scatter.argtypes = [P, i32, i32, i32, P, P, i32, P, P]
+    L.moe_ceiling_gather.argtypes = [P, i32, i32, i32, P, i32, i32, P, P]
+    for f in (L.moe_ceiling_read, L.moe_ceiling_write, L.moe_ceiling_scatter, L.moe_ceiling_gather):
+        f.restype = i32
+    return L
+
+
+def _checked(rc: int, what: str):
+    if rc != 0:
+        raise RuntimeError(f"{what} failed with status {rc}")
+
+
+def routed_rows(moe, S: int, K: int, E: int, R: int, dev, seed: int = 1):
+    """Receive rows [S,K] of a seeded uniform routing (moe_layout's pos)."""
+    import numpy as np
+    import torch
+    from workloads import uniform_distinct_routing
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, 99])))
+    idx = torch.from_numpy(uniform_distinct_routing(rng, S, E, K)).to(dev)
+    desc = moe.LayoutDesc(S, K, E, R)
+    lay = moe.moe_layout(desc, idx)
+    torch.cuda.synchronize()
+    return lay.pos
+
+
+class Patterns:
+    """Launchers for the four pattern kernels on torch's current stream."""
+
+    def __init__(self, dev):
+        import torch
+        self.L = ceiling_lib()
+        self.dev = dev
+        self.sink = torch.zeros(4, dtype=torch.int32, device=dev)
+
+    def _s(self):
+        import torch
+        return ctypes_stream(torch.cuda.current_stream(self.dev))
+
+    def read(self, buf, v, w, kind):
+        nb = buf.numel() * buf.element_size()
+        return lambda: _checked(self.L.moe_ceiling_read(buf.data_ptr(), nb, v, w, LOAD_KINDS[kind],
+                                                        self.sink.data_ptr(), self._s()), "read")
+
+    def write(self, buf, v, w, kind):
+        nb = buf.numel() * buf.element_size()
+        return lambda: _checked(self.L.moe_ceiling_write(buf.data_ptr(), nb, v, w, STORE_KINDS[kind], self._s()),
+                                "write")
+
+    def scatter(self, src, rows, dst, scales=None):
+        S, K = rows.shape
+        in_rb = src.shape[1] * src.element_size()
+        out_rb = dst.shape[1] * dst.element_size()
+        sp = scales.data_ptr() if scales is not None else None
+        return lambda: _checked(self.L.moe_ceiling_scatter(src.data_ptr(), S, in_rb, K, rows.data_ptr(),
+                                                           dst.data_ptr(), out_rb, sp, self._s()), "scatter")
+
+    def gather(self, y, rows, out, v=1, kind="sc1"):
+        S, K = rows.shape
+        rb = y.shape[1] * y.element_size()
+        return lambda: _checked(self.L.moe_ceiling_gather(y.data_ptr(), S, rb, K, rows.data_ptr(), v,
+                                                          STORE_KINDS[kind], out.data_ptr(), self._s()), "gather")
+
+
+def ctypes_stream(stream):
+    return stream.cuda_stream
+
+
+def _gbps(nbytes: int, ms: float) -> float:
+    return round(nbytes / (ms * 1e-3) / 1e9, 1)
+
+
+def ceiling_sweep(moe, dev, iters: int = 30):
+    """Pattern ceilings at >= 1 GiB per launch: streaming read and write by
+    workgroup shape and cache policy, the dispatch scatter (FP8 and bf16 row
+    bytes, K = 8) and the combine gather (K = 8, 1 or 2 KiB per wave, by
+    output store)."""
+    import torch
+    pat = Patterns(dev)
+    res = {"unit": "GB/s", "iters": iters, "read": {}, "write": {}}
+    big = torch.ones(1 << 28, dtype=torch.float32, device=dev)            # 1 GiB
+    nb = big.numel() * 4
+    for v, w in ((1, 1), (4, 1), (16, 1), (1, 4), (4, 4), (16, 4)):
+        for kind in ("plain", "nt"):
+            ms = time_calls(pat.read(big, v, w, kind), iters, 5)
+            res["read"][f"{v}KiB/wave x{w} waves/{kind}"] = _gbps(nb, ms)
+    for v, w in ((1, 1), (4, 1), (1, 4), (4, 4)):
+        for kind in ("plain", "nt", "sc1"):
+            ms = time_calls(pat.write(big, v, w, kind), iters, 5)
+            res["write"][f"{v}KiB/wave x{w} waves/{kind}"] = _gbps(nb, ms)
+    del big
+    S, K, H, E, R = 16384, 8, 7168, 256, 8
+    rows = routed_rows(moe, S, K, E, R, dev)
+    src = torch.ones((S, 2 * H), dtype=torch.uint8, device=dev)
+    out8 = torch.empty((S * K, H), dtype=torch.uint8, device=dev)
+    sc8 = torch.empty((S * K, H // 128), dtype=torch.float32, device=dev)
+    b8 = S * 2 * H + S * K * (H + 4 * (H // 128))
+    ms = time_calls(pat.scatter(src, rows, out8, sc8), iters, 5)
+    res["scatter_fp8_rows"] = {"shape": f"S={S} K={K} H={H}: read 2 KiB, write 1 KiB x {K} + scales",
+                               "bytes": b8, "gbps": _gbps(b8, ms)}
+    del out8, sc8
+    out16 = torch.empty((S * K, 2 * H), dtype=torch.uint8, device=dev)
+    b16 = S * 2 * H + S * K * 2 * H
+    ms = time_calls(pat.scatter(src, rows, out16), iters, 5)
+    res["scatter_bf16_rows"] = {"shape": f"S={S} K={K} H={H}: read 1 KiB, write 1 KiB x {K}",
+                                "bytes": b16, "gbps": _gbps(b16, ms)}
+    y = out16
+    out = torch.empty((S, 2 * H), dtype=torch.uint8, device=dev)
+    bg = S * K * 2 * H + S * 2 * H
+    res["gather"] = {"shape": f"S={S} K={K} H={H}: {K} routed rows in, one row out", "bytes": bg}
+    for v in (1, 2):
+        for kind in ("plain", "nt", "sc1"):
+            ms = time_calls(pat.gather(y, rows, out, v, kind), iters, 5)
+            res["gather"][f"{v}KiB/wave/{kind}"] = _gbps(bg, ms)
+    # the same gather from contiguous planes (row = k*S + t): no routing
+    planes = (torch.arange(K, device=dev, dtype=torch.int32)[None, :] * S
+              + torch.arange(S, device=dev, dtype=torch.int32)[:, None]).contiguous()
+    ms = time_calls(pat.gather(y, planes, out, 1, "sc1"), iters, 5)
+    res["gather"]["planes 1KiB/wave/sc1"] = _gbps(bg, ms)
+    del src, out16, y, out
+    return res
+
+
+def pattern_vs_product(moe, run, dev, iters: int = 30):
+    """The product dispatch and combine of this run next to the pattern kernels
+    that move the same bytes with the same rows (no arithmetic), timed back to
+    back on the same buffers: each kernel's fraction of its own pattern
+    ceiling."""
+    import torch
+    pat = Patterns(dev)
+    cfg = run.cfg
+    rows = run.buf.layout.pos
+    _, db, cb = run.bytes()
+    out = {}
+    hid_u8 = run.hidden.view(torch.uint8)
+    recv_u8 = run.buf.recv.view(torch.uint8)
+    scat = pat.scatter(hid_u8, rows, recv_u8, run.buf.recv_scales)
+    gath = pat.gather(run.expert_out.view(torch.uint8), rows, run.buf.out.view(torch.uint8), 1, "sc1")
+    t_d = time_calls(run.dispatch_call, iters, 5)
+    t_sc = time_calls(scat, iters, 5)
+    t_c = time_calls(run.combine_call, iters, 5)
+    t_g = time_calls(gath, iters, 5)
+    # restore the product's outputs (the pattern kernels overwrote them)
+    run.step()
+    torch.cuda.synchronize()
+    out["dispatch"] = {"kernel_us": round(t_d * 1e3, 2), "pattern_us": round(t_sc * 1e3, 2),
+                       "pattern": "moe_ceiling_scatter with the same rows and row bytes",
+                       "kernel_gbps": _gbps(db, t_d), "pattern_gbps": _gbps(db, t_sc),
+                       "kernel_over_pattern": round(t_sc / t_d, 4)}
+    out["combine"] = {"kernel_us": round(t_c * 1e3, 2), "pattern_us": round(t_g * 1e3, 2),
+                      "pattern": "moe_ceiling_gather with the same rows, SC1 output store",
+                      "kernel_gbps": _gbps(cb, t_c), "pattern_gbps": _gbps(cb, t_g),
+                      "kernel_over_pattern": round(t_g / t_c, 4)}
+    out["note"] = "back-to-back launches of one kernel; bytes are the product's algorithmic bytes"
+    return out
+
+
 def cpu_baseline(cfg, budget_s: float = 12.0):
     """The CPU oracle (single-threaded C) on the same workload: layout, dispatch
     and combine of full batches, repeated until ~budget_s of work."""
@@ -495,9 +711,12 @@ def main(argv=None):
     ap.add_argument("--decode-iters", type=int, default=500)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
-    ap.add_argument("--cu-budgets", default="32,64,128,256",
+    ap.add_argument("--cu-budgets", default="16,32,64,128,256",
                     help="comma-separated CU counts for the CU-limited-stream sweep ('' to skip)")
     ap.add_argument("--calib-copy", action="store_true")
+    ap.add_argument("--ceilings", action="store_true",
+                    help="time only the pattern-ceiling kernels (>= 1 GiB per launch) and the prefill "
+                         "dispatch / combine against their own patterns; print one JSON object")
     ap.add_argument("--only-decode", action="store_true",
                     help="time only the decode call (S=128) and print its JSON object")
     ap.add_argument("--no-percentiles", action="store_true",
@@ -526,6 +745,14 @@ def main(argv=None):
     if args.only_balanced:
         print(json.dumps(balanced_numbers(moe, CONFIGS["skew"], dev)), flush=True)
         return
+    if args.ceilings:
+        res = {"ceilings": ceiling_sweep(moe, dev)}
+        for name in ("prefill", "skew"):
+            r = Run(moe, CONFIGS[name], dev)
+            res[f"{name}_vs_pattern"] = pattern_vs_product(moe, r, dev)
+            del r
+        print(json.dumps(res), flush=True)
+        return
     cfg = CONFIGS[args.config]
     run = Run(moe, cfg, dev)
     lb, db, cb = run.bytes()
@@ -549,6 +776,7 @@ def main(argv=None):
         ref = streaming_reference(cfg, dev)
         ref["kernel_over_reference"] = round(achieved / ref["gbps"], 3)
         roofline["streaming_reference"] = ref
+        roofline["own_pattern"] = pattern_vs_product(moe, run, dev)
 
     extra = {"layout_us": round(t["layout_ms"] * 1e3, 2), "dispatch_us": round(t["dispatch_ms"] * 1e3, 2),
              "combine_us": round(t["combine_ms"] * 1e3, 2), "dispatch_gbps": round(d_gbps, 1),
@@ -558,11 +786,17 @@ def main(argv=None):
 
     drun = None if args.no_decode else Run(moe, CONFIGS["decode"], dev)
     decode = None if args.no_decode else decode_numbers(moe, CONFIGS["decode"], dev, args.decode_iters, drun)
-    pct = None if args.no_percentiles else percentile_numbers(
-        run, drun, trun=None if args.no_decode else Run(moe, CONFIGS["tiny"], dev))
-    also = None
+    also, srun = None, None
     if not args.no_decode and cfg.name == "prefill":
-        also = shape_numbers(moe, CONFIGS["skew"], dev)
+        srun = Run(moe, CONFIGS["skew"], dev)
+        also = shape_numbers(moe, CONFIGS["skew"], dev, run=srun)
+    pct = None if args.no_percentiles else percentile_numbers(
+        run, drun, trun=None if args.no_decode else Run(moe, CONFIGS["tiny"], dev), srun=srun)
+    if pct is not None:
+        extra.update(cold_dc(pct["batch"], db + cb))
+        if also is not None:
+            also.update(cold_dc(pct["skew"], also["bytes"]["dispatch"] + also["bytes"]["combine"]))
+    del srun
     balanced = None if args.no_decode else balanced_numbers(moe, CONFIGS["skew"], dev)
     budgets = [int(x) for x in args.cu_budgets.split(",") if x.strip()]
     cu_budget = cu_budget_numbers(moe, run, budgets) if budgets else None

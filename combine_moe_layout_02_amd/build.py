@@ -1,6 +1,7 @@
-"""Builds libmoe_ep.so in-tree with hipcc for gfx950 (MI355X).
+"""Builds libmoe_ep.so in-tree with hipcc for gfx950 (MI355X), and beside it
+libmoe_ceilings.so, the pattern-ceiling kernels the benchmark times.
 
-Each HIP source is compiled to an object in parallel, then linked into one
+Each HIP source is compiled to an object in parallel, then linked into its
 shared library next to this file.  Flags:
   -ffp-contract=off            no implicit fused multiply-adds: combine's fma
                                chain is spelled out, nothing else is fused
@@ -20,6 +21,8 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libmoe_ep.so")
 SOURCES = ["api.hip", "layout.hip", "dispatch.hip", "combine.hip", "fused.hip", "balance.hip", "padding.hip"]
+CEIL_LIB = os.path.join(HERE, "libmoe_ceilings.so")
+CEIL_SOURCES = ["ceilings.hip"]
 ARCH = "gfx950"
 
 COMMON_FLAGS = [
@@ -33,8 +36,7 @@ def hipcc() -> str:
     return os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source for gfx950 and link libmoe_ep.so (always rebuilds)."""
+def _build_lib(lib: str, sources, verbose: bool) -> str:
     with tempfile.TemporaryDirectory(prefix="moe_ep_build_") as tmp:
         def compile_one(src: str) -> str:
             obj = os.path.join(tmp, src + ".o")
@@ -48,15 +50,25 @@ def build(verbose: bool = False) -> str:
                 print(out)
             return obj
 
-        with concurrent.futures.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-            objs = list(ex.map(compile_one, SOURCES))
-        tmp_lib = LIB + ".tmp"
+        with concurrent.futures.ThreadPoolExecutor(max_workers=len(sources)) as ex:
+            objs = list(ex.map(compile_one, sources))
+        tmp_lib = lib + ".tmp"
         cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp_lib, *objs]
         r = subprocess.run(cmd, capture_output=True, text=True)
         if r.returncode != 0:
             raise RuntimeError(f"link failed:\n{r.stdout}{r.stderr}")
-        os.replace(tmp_lib, LIB)
-    return LIB
+        os.replace(tmp_lib, lib)
+    return lib
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source for gfx950 and link libmoe_ep.so and
+    libmoe_ceilings.so (always rebuilds).  Returns the path of libmoe_ep.so."""
+    with concurrent.futures.ThreadPoolExecutor(max_workers=2) as ex:
+        main = ex.submit(_build_lib, LIB, SOURCES, verbose)
+        ceil = ex.submit(_build_lib, CEIL_LIB, CEIL_SOURCES, verbose)
+        ceil.result()
+        return main.result()
 
 
 if __name__ == "__main__":

@@ -165,3 +165,39 @@ def test_status_strings(moe):
     for s in range(6):
         assert moe.moe_status_str(s).startswith("MOE_")
     assert moe.moe_status_str(99) == "unknown moe_status"
+
+
+CEIL_HEADER = os.path.join(ROOT, "include", "moe_ceilings.h")
+
+
+def test_ceiling_library_exports_and_rejects_bad_arguments():
+    """The pattern-ceiling library exports every call its header declares and
+    refuses bad shapes and misaligned pointers before any launch."""
+    from combine_moe_layout_02_amd.build import CEIL_LIB
+    if not os.path.exists(CEIL_LIB):
+        import __graft_entry__
+        __graft_entry__.build()
+    text = re.sub(r"/\*.*?\*/", "", open(CEIL_HEADER).read(), flags=re.S)
+    names = sorted(set(re.findall(r"\b(moe_ceiling_[a-z_0-9]+)\s*\(", text)))
+    assert names == ["moe_ceiling_gather", "moe_ceiling_read", "moe_ceiling_scatter", "moe_ceiling_write"]
+    import bench
+    L = bench.ceiling_lib()
+    for n in names:
+        assert getattr(L, n) is not None
+    ERR = 1
+    P = ctypes.c_void_p
+    A = FAKE
+    assert L.moe_ceiling_read(None, 1 << 20, 1, 1, 0, P(A), None) == ERR
+    assert L.moe_ceiling_read(P(A + 4), 1 << 20, 1, 1, 0, P(A), None) == ERR        # misaligned
+    assert L.moe_ceiling_read(P(A), 1000, 1, 1, 0, P(A), None) == ERR                 # not whole KiB
+    assert L.moe_ceiling_read(P(A), 1 << 20, 3, 1, 0, P(A), None) == ERR              # 3 vectors per lane
+    assert L.moe_ceiling_read(P(A), 1 << 20, 1, 1, 2, P(A), None) == ERR              # unknown load kind
+    assert L.moe_ceiling_read(P(A), 3 << 10, 1, 2, 0, P(A), None) == ERR              # 3 KiB over 2-wave groups
+    assert L.moe_ceiling_write(P(A), 1 << 20, 1, 17, 0, None) == ERR                  # too many waves
+    assert L.moe_ceiling_write(P(A), 1 << 20, 1, 1, 3, None) == ERR                   # unknown store kind
+    assert L.moe_ceiling_scatter(P(A), 8, 3000, 8, P(A), P(A), 1024, None, None) == ERR   # row ratio
+    assert L.moe_ceiling_scatter(P(A), 8, 1536, 8, P(A), P(A), 1536, None, None) == ERR   # not whole KiB
+    assert L.moe_ceiling_scatter(P(A), 8, 2048, 3, P(A), P(A), 1024, None, None) == ERR   # K = 3
+    assert L.moe_ceiling_gather(P(A), 8, 3072, 8, P(A), 2, 0, P(A), None) == ERR         # 3 KiB in 2 KiB chunks
+    assert L.moe_ceiling_gather(P(A), 0, 1024, 8, P(A), 1, 0, P(A), None) == ERR         # empty
+    assert L.moe_ceiling_gather(P(A), 8, 1024, 8, None, 1, 0, P(A), None) == ERR         # no rows
