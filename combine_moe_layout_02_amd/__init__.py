@@ -25,7 +25,7 @@ MOE_FLAG_BAD_EXPERT, MOE_FLAG_CAPACITY, MOE_FLAG_UNBALANCED = 1, 2, 4
 EXPORTED = ("moe_max_recv_rows", "moe_layout_workspace_bytes", "moe_layout", "moe_dispatch",
             "moe_layout_dispatch", "moe_combine", "moe_layout_balanced_workspace_bytes", "moe_layout_balanced",
             "moe_zero_padding", "moe_stream_create_cu_limited", "moe_stream_create_cu_range", "moe_stream_destroy",
-            "moe_status_str")
+            "moe_status_str", "moe_layout_noalloc")
 
 
 class MoeError(RuntimeError):
@@ -84,6 +84,8 @@ def _load():
     L.moe_stream_destroy.restype = ctypes.c_int
     L.moe_status_str.argtypes = [ctypes.c_int32]
     L.moe_status_str.restype = ctypes.c_char_p
+    L.moe_layout_noalloc.argtypes = [D, P, B, P]
+    L.moe_layout_noalloc.restype = ctypes.c_int
     return L
 
 
@@ -252,6 +254,19 @@ def moe_layout(desc: LayoutDesc, topk_idx: torch.Tensor, layout: Optional[Layout
                          0 if ws is None else ws.numel(), _stream(stream, dev))
     if rc != MOE_OK:
         raise MoeError(rc, "moe_layout")
+    return layout
+
+
+def moe_layout_noalloc(desc: LayoutDesc, topk_idx: torch.Tensor, layout: Layout, stream=None) -> Layout:
+    """moe_layout with the library's own per-GPU scratch instead of a
+    workspace: the C call allocates nothing (the output tensors of `layout`
+    are the caller's; its workspace, if any, is not used)."""
+    dev = topk_idx.device
+    _check(topk_idx, "topk_idx", torch.int32, (desc.S, desc.K))
+    d, b = desc.c(), layout.c()
+    rc = _lib.moe_layout_noalloc(ctypes.byref(d), _ptr(topk_idx), ctypes.byref(b), _stream(stream, dev))
+    if rc != MOE_OK:
+        raise MoeError(rc, "moe_layout_noalloc")
     return layout
 
 

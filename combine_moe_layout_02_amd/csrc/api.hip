@@ -4,6 +4,7 @@
 #include <hip/hip_ext.h>
 #include <stdint.h>
 
+#include <atomic>
 #include <vector>
 
 #include "moe_ep.h"
@@ -14,7 +15,39 @@ hipError_t launch_zero_padding(const int32_t *src, int rows, int row_bytes, void
                                hipStream_t s);  // padding.hip
 }
 
+// Scratch of moe_layout_noalloc, for callers that cannot allocate: the
+// two-launch layout's per-tile histograms and flags, in a file-scope device
+// array.  Each GPU the library runs on holds its own copy until the process
+// ends.  Host code never uses the array's name as an address: each device's
+// copy is looked up once with hipGetSymbolAddress (scratch_ptr below).
+constexpr size_t kNoAllocScratchBytes = size_t(4) << 20;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
 namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<void *> g_scratch_ptr[kMaxDevices];
+
+// The current device's copy of `scratch` (resolved on the first call on that
+// device, with it current), or null with st set.
+void *scratch_ptr(moe_status &st) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+        (void)hipGetLastError();
+        st = MOE_ERR_HIP;
+        return nullptr;
+    }
+    void *p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (p == nullptr) {
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) {
+            (void)hipGetLastError();
+            st = MOE_ERR_HIP;
+            return nullptr;
+        }
+        g_scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+    return p;
+}
 
 bool desc_ok(const moe_layout_desc *d) {
     if (d->S < 0 || d->K < 1 || d->K > moe::kMaxK || d->E < 1 || d->E > moe::kMaxE || d->R < 1 ||
@@ -142,6 +175,24 @@ moe_status moe_layout(const moe_layout_desc *desc, const int32_t *topk_idx, cons
                       void *workspace, size_t workspace_bytes, void *stream) {
     moe::LayoutArgs a;
     const moe_status st = prepare_layout(desc, topk_idx, out, workspace, workspace_bytes, a);
+    if (st != MOE_OK) return st;
+    return moe::launch_layout(a, static_cast<hipStream_t>(stream)) == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+moe_status moe_layout_noalloc(const moe_layout_desc *desc, const int32_t *topk_idx, const moe_layout_bufs *out,
+                              void *stream) {
+    if (desc == nullptr || out == nullptr) return MOE_ERR_NULL;
+    if (!desc_ok(desc) || max_rows(desc) < 0) return MOE_ERR_SHAPE;
+    const size_t need = moe::layout_workspace_bytes(static_cast<int64_t>(desc->S) * desc->K, desc->E);
+    if (need > kNoAllocScratchBytes) return MOE_ERR_WORKSPACE;
+    void *ws = nullptr;
+    if (need > 0) {
+        moe_status st = MOE_OK;
+        ws = scratch_ptr(st);
+        if (ws == nullptr) return st;
+    }
+    moe::LayoutArgs a;
+    const moe_status st = prepare_layout(desc, topk_idx, out, ws, need, a);
     if (st != MOE_OK) return st;
     return moe::launch_layout(a, static_cast<hipStream_t>(stream)) == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }

@@ -139,6 +139,20 @@ moe_status moe_layout(const moe_layout_desc *desc, const int32_t *topk_idx,
                       const moe_layout_bufs *out, void *workspace, size_t workspace_bytes,
                       void *stream);
 
+/* moe_layout without a workspace argument, for callers that cannot allocate
+ * device memory (code under graph capture, tight serving loops, harnesses that
+ * forbid allocation).  Same results as moe_layout.  The two-launch form
+ * (S*K > 32768) keeps its per-tile histograms in a device array inside the
+ * library, 4 MiB per GPU, held from the first call on a GPU until the process
+ * ends: MOE_ERR_WORKSPACE when moe_layout_workspace_bytes exceeds 4 MiB (about
+ * 4M entries at E = 1024, 16M at E = 256).  Every call on one GPU shares that
+ * array, so calls that overlap in time on one GPU (other streams, other host
+ * threads) race; calls on one stream are fine.  The array needs no clearing:
+ * each call writes every histogram and flag it reads.  The current device must
+ * be the stream's device.  No allocation, free or host sync. */
+moe_status moe_layout_noalloc(const moe_layout_desc *desc, const int32_t *topk_idx,
+                              const moe_layout_bufs *out, void *stream);
+
 /* Dispatch: row pos[t,k] of the receive buffer gets token t's hidden row.
  *   hidden      [S,H] bf16 device, 16-byte aligned, H % 8 == 0.
  *   topk_idx    [S,K] int32; the expert ids already folded into `layout`
