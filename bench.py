@@ -22,6 +22,8 @@ padded to 128 rows) is timed too.
   --calib-copy       run only a plain device copy of known size (for scaling
                      rocprofv3 FETCH_SIZE / WRITE_SIZE counters)
   --ceilings         run only the pattern-ceiling kernels (libmoe_ceilings.so)
+  --summarize DIR    turn a profiling run's rocprofv3 CSVs into markdown tables
+                     and profiles/traffic.json (CPU only)
   --no-cpu-baseline  skip timing the CPU oracle
   --no-decode        skip the decode, balanced-layout and skewed-batch numbers
   --no-percentiles   skip the percentile pass and the streaming reference
@@ -691,6 +693,161 @@ def cpu_model() -> str:
     return "unknown"
 
 
+# ---------------------------------------------------------------------------
+# profile summaries (rocprofv3 CSV -> markdown tables and profiles/traffic.json)
+# ---------------------------------------------------------------------------
+
+ROLE_SOURCES = {"layout": ["layout.hip", "small_layout.h", "moe_kernels.h"],
+                "dispatch": ["dispatch.hip", "moe_kernels.h"],
+                "combine": ["combine.hip", "moe_kernels.h"]}
+
+
+def _role(kernel_name: str):
+    for key, role in (("k_layout_dispatch", "layout"), ("k_layout", "layout"), ("k_dispatch", "dispatch"),
+                      ("k_combine", "combine")):
+        if key in kernel_name:
+            return role
+    return None
+
+
+def _short(kernel_name: str) -> str:
+    import re
+    m = re.search(r"(k_[A-Za-z0-9_]+(?:<[^>]*>)?)\(", kernel_name)
+    return m.group(1) if m else kernel_name
+
+
+def _csv_rows(path: str):
+    import csv
+    with open(path) as f:
+        return list(csv.DictReader(f))
+
+
+def _find(dirpath: str, suffix: str):
+    for name in sorted(os.listdir(dirpath)):
+        if name.endswith(suffix):
+            return os.path.join(dirpath, name)
+    raise FileNotFoundError(f"no *{suffix} in {dirpath}")
+
+
+def _counter_kib(dirpath: str):
+    """Median counter value (KiB) per dispatch, by kernel name."""
+    import numpy as np
+    per = {}
+    for r in _csv_rows(_find(dirpath, "_counter_collection.csv")):
+        per.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+    return {k: float(np.median(v)) for k, v in per.items()}
+
+
+def summarize_profiles(dirpath: str, write_traffic: bool = True) -> str:
+    """Markdown summary of one profiling run (the layout written by the
+    commands in the returned text's header) and, with write_traffic, the HBM
+    bytes per launch of every dispatch and combine kernel into
+    profiles/traffic.json, keyed by the sources' SHA-256."""
+    import numpy as np
+    from workloads import CONFIGS
+    calib = {}
+    for P in ("FETCH_SIZE", "WRITE_SIZE"):
+        kib = _counter_kib(os.path.join(dirpath, f"calib_{P}"))
+        copy_kib = max(kib.values())            # the 1 GiB copy is the largest mover of the run
+        calib[P] = ((1 << 30) / 1024.0 / copy_kib, copy_kib)
+    out = ["# All five workloads: per-kernel duration, HBM traffic and per-call percentiles\n",
+           "MI355X (gfx950), one GPU, ROCm 7.2, rocprofv3, one box, one run of each command below per",
+           "workload `C` in tiny, prefill, decode, skew, dsmoe16b (`R` = repo root on the GPU box, run",
+           "from /tmp):\n",
+           "    python3 $R/bench.py --config C --no-cpu-baseline --no-decode --cu-budgets \"\" > $R/gpurun_out/prof/bench_C.json",
+           "    rocprofv3 --kernel-trace --stats --output-format csv -d $R/gpurun_out/prof/kt_C -o C \\",
+           "        -- python3 $R/bench.py --config C --steps 20 --warmup 5 --no-cpu-baseline --no-decode --no-percentiles --cu-budgets \"\"",
+           "    timeout -s KILL 150 rocprofv3 --pmc FETCH_SIZE --output-format csv -d $R/gpurun_out/prof/pmc_FETCH_SIZE_C -o C \\",
+           "        -- python3 $R/bench.py --config C --steps 3 --warmup 1 --no-cpu-baseline --no-decode --no-percentiles --cu-budgets \"\"",
+           "    (the same with WRITE_SIZE; calibration: each counter over `python3 $R/bench.py --calib-copy`,",
+           "     a plain 1 GiB device copy, into $R/gpurun_out/prof/calib_FETCH_SIZE and calib_WRITE_SIZE)",
+           "    python3 bench.py --summarize gpurun_out/prof    (this file, and profiles/traffic.json)\n",
+           f"Counter scaling: FETCH_SIZE x {calib['FETCH_SIZE'][0]:.6f}, WRITE_SIZE x {calib['WRITE_SIZE'][0]:.6f} "
+           "(what each counter reads",
+           "for the 1 GiB copy).  Algorithmic bytes are those bench.py reports: layout 8*S*K + 4*max_recv,",
+           "dispatch 2*S*H + placed*rowbytes + 12*S*K, combine placed*2H + 8*S*K + 2*S*H (+ 2*S*H shared);",
+           "padding rows excluded.  GB/s and % of 8 TB/s use the kernel-trace average duration.  Percentiles",
+           "are per call, HIP events around each call, 100 calls: warm = back to back, cold = right after a",
+           "read-only pass over 512 MiB written once beforehand (no dirty lines left for the timed calls).\n"]
+    traffic = {"about": "HBM bytes per launch from rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE (KiB per dispatch), "
+                        "each scaled by what the same counter reads for a plain 1 GiB device copy "
+                        "(bench.py --calib-copy). Valid only while the listed sources hash to source_sha256. "
+                        "Written by bench.py --summarize.",
+               "calibration": {"copy_bytes": 1 << 30, "fetch_size_kib": calib["FETCH_SIZE"][1],
+                               "write_size_kib": calib["WRITE_SIZE"][1],
+                               "fetch_factor": round(calib["FETCH_SIZE"][0], 6),
+                               "write_factor": round(calib["WRITE_SIZE"][0], 6)}}
+    for name, cfg in CONFIGS.items():
+        kt = os.path.join(dirpath, f"kt_{name}")
+        if not os.path.isdir(kt):
+            continue
+        with open(os.path.join(dirpath, f"bench_{name}.json")) as f:
+            line = json.loads(f.read().strip().splitlines()[-1])
+        k = line["kernels"]
+        alg = k["bytes"]
+        stats = {r["Name"]: float(r["AverageNs"]) for r in _csv_rows(_find(kt, "_kernel_stats.csv"))}
+        fetch = _counter_kib(os.path.join(dirpath, f"pmc_FETCH_SIZE_{name}"))
+        write = _counter_kib(os.path.join(dirpath, f"pmc_WRITE_SIZE_{name}"))
+        desc = (f"S={cfg.S}, H={cfg.H}, E={cfg.E}, K={cfg.K}, R={cfg.R}, {'FP8' if cfg.fp8 else 'bf16'} dispatch"
+                + ({1: f", segments padded to a multiple of {cfg.pad_rows}",
+                    2: f", capacity {cfg.pad_rows} rows per expert"}.get(cfg.pad_mode, ""))
+                + (", shared-expert output" if cfg.shared else "") + f", {cfg.routing} routing")
+        out.append(f"## {name}: {desc}\n")
+        dc = k["dispatch_plus_combine_gbps"]
+        out.append(f"bench.py line: step {line['ms_per_step'] * 1e3:.1f} µs, whole step {line['value']:.0f} GB/s; "
+                   f"dispatch + combine {dc:.0f} GB/s = {100 * dc / HBM_PEAK_GBPS:.1f} % of 8 TB/s (HIP events).\n")
+        out.append("| kernel | role | avg µs (trace) | algorithmic B | GB/s | % of 8 TB/s | HBM read B | HBM write B "
+                   "| traffic / algorithmic |")
+        out.append("|---|---|---|---|---|---|---|---|---|")
+        by_role = {}
+        for kname, ns in stats.items():
+            role = _role(kname)
+            if role is None:
+                continue
+            rd = fetch.get(kname, float("nan")) * 1024 * calib["FETCH_SIZE"][0]
+            wr = write.get(kname, float("nan")) * 1024 * calib["WRITE_SIZE"][0]
+            r = by_role.setdefault(role, {"names": [], "ns": 0.0, "rd": 0.0, "wr": 0.0, "fkib": 0.0, "wkib": 0.0})
+            r["names"].append(kname)
+            r["ns"] += ns
+            r["rd"] += rd
+            r["wr"] += wr
+            r["fkib"] += fetch.get(kname, float("nan"))
+            r["wkib"] += write.get(kname, float("nan"))
+        for role in ("layout", "dispatch", "combine"):
+            if role not in by_role:
+                continue
+            r = by_role[role]
+            a = alg[role]
+            us = r["ns"] / 1e3
+            gbps = a / (us * 1e-6) / 1e9
+            out.append(f"| {' + '.join(_short(n) for n in r['names'])} | {role} | {us:.2f} | {a:,} | {gbps:,.0f} | "
+                       f"{100 * gbps / HBM_PEAK_GBPS:.1f} | {r['rd']:,.0f} | {r['wr']:,.0f} | "
+                       f"{(r['rd'] + r['wr']) / a:.4f} |")
+            if role in ("dispatch", "combine") and len(r["names"]) == 1:
+                srcs = ROLE_SOURCES[role]
+                traffic[f"{role}/{name}"] = {
+                    "kernel": _short(r["names"][0]), "sources": srcs, "source_sha256": sources_sha256(srcs),
+                    "fetch_size_kib": round(r["fkib"], 1), "write_size_kib": round(r["wkib"], 1),
+                    "read_bytes": int(round(r["rd"])), "write_bytes": int(round(r["wr"])),
+                    "bytes_per_launch": int(round(r["rd"] + r["wr"])), "algorithmic_bytes_per_launch": a,
+                    "traffic_over_algorithmic": round((r["rd"] + r["wr"]) / a, 4),
+                    "kernel_trace_avg_us": round(us, 2)}
+        pct = (line.get("percentiles") or {}).get("batch")
+        if pct:
+            out.append("")
+            out.append("| call | warm p10 / p50 / p90 µs | cold p10 / p50 / p90 µs |")
+            out.append("|---|---|---|")
+            for c in pct["calls"]:
+                w_, c_ = pct["warm_us"][c], pct["cold_us"][c]
+                out.append(f"| {c} | {w_[0]:.2f} / {w_[1]:.2f} / {w_[2]:.2f} | {c_[0]:.2f} / {c_[1]:.2f} / {c_[2]:.2f} |")
+        out.append("")
+    if write_traffic:
+        with open(TRAFFIC_FILE, "w") as f:
+            json.dump(traffic, f, indent=1)
+            f.write("\n")
+    return "\n".join(out)
+
+
 def calib_copy(nbytes: int = 1 << 30):
     """A plain device-to-device copy of a known size, for counter scaling."""
     import torch
@@ -714,6 +871,9 @@ def main(argv=None):
     ap.add_argument("--cu-budgets", default="16,32,64,128,256",
                     help="comma-separated CU counts for the CU-limited-stream sweep ('' to skip)")
     ap.add_argument("--calib-copy", action="store_true")
+    ap.add_argument("--summarize", metavar="DIR",
+                    help="summarize a profiling run's rocprofv3 CSVs (markdown to stdout) and write "
+                         "profiles/traffic.json; runs on the CPU")
     ap.add_argument("--ceilings", action="store_true",
                     help="time only the pattern-ceiling kernels (>= 1 GiB per launch) and the prefill "
                          "dispatch / combine against their own patterns; print one JSON object")
@@ -732,6 +892,9 @@ def main(argv=None):
         sys.exit(2)
     if args.calib_copy:
         calib_copy()
+        return
+    if args.summarize:
+        print(summarize_profiles(args.summarize))
         return
 
     import torch
