@@ -489,7 +489,9 @@ def ceiling_lib():
     L.moe_ceiling_write.argtypes = [P, i64, i32, i32, i32, P]
     L.moe_ceiling_scatter.argtypes = [P, i32, i32, i32, P, P, i32, P, P]
     L.moe_ceiling_gather.argtypes = [P, i32, i32, i32, P, i32, i32, P, P]
-    for f in (L.moe_ceiling_read, L.moe_ceiling_write, L.moe_ceiling_scatter, L.moe_ceiling_gather):
+    L.moe_ceiling_gather_persistent.argtypes = [P, i32, i32, i32, P, i32, i32, i32, P, P]
+    for f in (L.moe_ceiling_read, L.moe_ceiling_write, L.moe_ceiling_scatter, L.moe_ceiling_gather,
+              L.moe_ceiling_gather_persistent):
         f.restype = i32
     return L
 
@@ -542,6 +544,13 @@ class Patterns:
         sp = scales.data_ptr() if scales is not None else None
         return lambda: _checked(self.L.moe_ceiling_scatter(src.data_ptr(), S, in_rb, K, rows.data_ptr(),
                                                            dst.data_ptr(), out_rb, sp, self._s()), "scatter")
+
+    def gather_persistent(self, y, rows, out, groups, waves, kind="sc1"):
+        S, K = rows.shape
+        rb = y.shape[1] * y.element_size()
+        return lambda: _checked(self.L.moe_ceiling_gather_persistent(
+            y.data_ptr(), S, rb, K, rows.data_ptr(), groups, waves, STORE_KINDS[kind], out.data_ptr(), self._s()),
+            "gather_persistent")
 
     def gather(self, y, rows, out, v=1, kind="sc1"):
         S, K = rows.shape
@@ -605,6 +614,11 @@ def ceiling_sweep(moe, dev, iters: int = 30):
               + torch.arange(S, device=dev, dtype=torch.int32)[:, None]).contiguous()
     ms = time_calls(pat.gather(y, planes, out, 1, "sc1"), iters, 5)
     res["gather"]["planes 1KiB/wave/sc1"] = _gbps(bg, ms)
+    n_cu = torch.cuda.get_device_properties(dev).multi_processor_count
+    for per_cu in (2, 4, 8):
+        for waves in (1, 4):
+            ms = time_calls(pat.gather_persistent(y, rows, out, n_cu * per_cu, waves, "sc1"), iters, 5)
+            res["gather"][f"persistent {per_cu} groups/CU x{waves} waves/sc1"] = _gbps(bg, ms)
     del src, out16, y, out
     return res
 
@@ -628,6 +642,12 @@ def pattern_vs_product(moe, run, dev, iters: int = 30):
     t_sc = time_calls(scat, iters, 5)
     t_c = time_calls(run.combine_call, iters, 5)
     t_g = time_calls(gath, iters, 5)
+    n_cu = torch.cuda.get_device_properties(dev).multi_processor_count
+    pers = {}
+    for per_cu, waves in ((4, 1), (8, 1), (2, 4), (4, 4)):
+        t_p = time_calls(pat.gather_persistent(run.expert_out.view(torch.uint8), rows, run.buf.out.view(torch.uint8),
+                                               n_cu * per_cu, waves, "sc1"), iters, 5)
+        pers[f"{per_cu} groups/CU x{waves} waves"] = round(t_p * 1e3, 2)
     # restore the product's outputs (the pattern kernels overwrote them)
     run.step()
     torch.cuda.synchronize()
@@ -638,7 +658,7 @@ def pattern_vs_product(moe, run, dev, iters: int = 30):
     out["combine"] = {"kernel_us": round(t_c * 1e3, 2), "pattern_us": round(t_g * 1e3, 2),
                       "pattern": "moe_ceiling_gather with the same rows, SC1 output store",
                       "kernel_gbps": _gbps(cb, t_c), "pattern_gbps": _gbps(cb, t_g),
-                      "kernel_over_pattern": round(t_g / t_c, 4)}
+                      "kernel_over_pattern": round(t_g / t_c, 4), "persistent_pattern_us": pers}
     out["note"] = "back-to-back launches of one kernel; bytes are the product's algorithmic bytes"
     return out
 

@@ -136,6 +136,103 @@ __global__ __launch_bounds__(kWave) void k_gather(const u32x4 *__restrict__ y, i
     }
 }
 
+// The gather pattern in persistent form: every wave walks (token, 1 KiB
+// chunk) units u = w, w + nwaves, ... (chunk-fastest, as above) and keeps the
+// next unit's K row loads in flight while it combines and stores the current
+// one.  A unit is tracked as (t, c) and advanced by whole strides, so no
+// division runs in the loop; both stay wave-uniform (scalar registers).
+struct Unit {
+    int t, c;
+};
+
+__device__ __forceinline__ Unit unit_next(Unit x, int dt, int dc, int nchunk) {
+    x.c += dc;
+    x.t += dt;
+    if (x.c >= nchunk) {
+        x.c -= nchunk;
+        x.t += 1;
+    }
+    return x;
+}
+
+template <int K>
+__device__ __forceinline__ void unit_rows(const int32_t *__restrict__ rows, Unit x, int (&p)[K]) {
+    const int32_t *pr = rows + static_cast<size_t>(x.t) * K;
+#pragma unroll
+    for (int k = 0; k < K; ++k) p[k] = pr[k];
+}
+
+// Gathers of one unit through buffer loads: each row chunk gets a descriptor
+// built in scalar registers (base at the chunk, 1 KiB long), and the lane's
+// byte offset is the only vector operand, so the loads need no per-load
+// vector address arithmetic.  An entry with no row gets a zero-length
+// descriptor: its load returns zeros without touching memory.
+constexpr int kCachePolicyNt = 1 << 1;
+
+template <int K>
+__device__ __forceinline__ void unit_gather(const u32x4 *__restrict__ y, int nvec, Unit x, const int (&p)[K],
+                                            u32x4 (&r)[K]) {
+    const int lane_off = static_cast<int>(threadIdx.x % kWave) * 16;
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+        const u32x4 *chunk = y + static_cast<size_t>(p[k] >= 0 ? p[k] : 0) * nvec + x.c * kWave;
+        const __amdgpu_buffer_rsrc_t d =
+            __builtin_amdgcn_make_buffer_rsrc(const_cast<u32x4 *>(chunk), 0, p[k] >= 0 ? kWave * 16 : 0, kBufferRsrcWord3);
+        r[k] = __builtin_amdgcn_raw_buffer_load_b128(d, lane_off, 0, kCachePolicyNt);
+    }
+}
+
+// Combines the K rows of one unit and stores the chunk.
+template <int K, int KIND>
+__device__ __forceinline__ void unit_store(const u32x4 (&r)[K], u32x4 *__restrict__ out, int nvec, Unit x) {
+    u32x4 acc = r[0];
+#pragma unroll
+    for (int k = 1; k < K; ++k) acc ^= r[k];
+    const int v = x.c * kWave + static_cast<int>(threadIdx.x % kWave);
+    store16<KIND>(acc, out + static_cast<size_t>(x.t) * nvec, static_cast<unsigned int>(v),
+                  static_cast<unsigned int>(nvec) * 16u);
+}
+
+template <int K, int KIND>
+__global__ __launch_bounds__(256) void k_gather_persistent(const u32x4 *__restrict__ y, int nvec,
+                                                           const int32_t *__restrict__ rows,
+                                                           u32x4 *__restrict__ out, int nchunk, int S) {
+    const int wpg = blockDim.x / kWave;
+    const int nwaves = gridDim.x * wpg;
+    const int w = blockIdx.x * wpg + __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    if (w >= S * nchunk) return;
+    const int dt = nwaves / nchunk, dc = nwaves % nchunk;
+    // Two register sets take turns: while one unit's gathers are combined and
+    // stored, the next unit's are in flight in the other set.  Past the last
+    // unit the prefetches repeat the current one, so no load sits behind a
+    // branch and the waits cover only the unit being combined.
+    Unit cur = {w / nchunk, w % nchunk};
+    int pa[K], pb[K];
+    u32x4 ra[K], rb[K];
+    unit_rows<K>(rows, cur, pa);
+    unit_gather<K>(y, nvec, cur, pa, ra);
+    Unit nxt = unit_next(cur, dt, dc, nchunk);
+    unit_rows<K>(rows, nxt.t < S ? nxt : cur, pb);
+    while (true) {
+        nxt = unit_next(cur, dt, dc, nchunk);
+        Unit nn = unit_next(nxt, dt, dc, nchunk);
+        unit_gather<K>(y, nvec, nxt.t < S ? nxt : cur, pb, rb);
+        unit_rows<K>(rows, nn.t < S ? nn : cur, pa);
+        __builtin_amdgcn_sched_barrier(0);   // the next unit's loads go out before this unit is combined
+        unit_store<K, KIND>(ra, out, nvec, cur);
+        if (nxt.t >= S) break;
+        cur = nxt;
+        nxt = nn;
+        nn = unit_next(nxt, dt, dc, nchunk);
+        unit_gather<K>(y, nvec, nxt.t < S ? nxt : cur, pa, ra);
+        unit_rows<K>(rows, nn.t < S ? nn : cur, pb);
+        __builtin_amdgcn_sched_barrier(0);
+        unit_store<K, KIND>(rb, out, nvec, cur);
+        if (nxt.t >= S) break;
+        cur = nxt;
+    }
+}
+
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 int32_t launched() { return hipGetLastError() == hipSuccess ? MOE_CEIL_OK : MOE_CEIL_ERR_HIP; }
@@ -260,5 +357,27 @@ extern "C" int32_t moe_ceiling_gather(const void *y, int32_t S, int32_t row_byte
     } else {
         CEIL_GATHER_KIND(2)
     }
+    return launched();
+}
+
+extern "C" int32_t moe_ceiling_gather_persistent(const void *y, int32_t S, int32_t row_bytes, int32_t K,
+                                                 const int32_t *rows, int32_t groups, int32_t waves_per_group,
+                                                 int32_t store_kind, void *out, void *stream) {
+    if (y == nullptr || rows == nullptr || out == nullptr || !aligned16(y) || !aligned16(out)) return MOE_CEIL_ERR_ARG;
+    if (S < 1 || row_bytes < 1024 || row_bytes % 1024 || groups < 1 || waves_per_group < 1 || waves_per_group > 4)
+        return MOE_CEIL_ERR_ARG;
+    const int nvec = row_bytes / 16, nchunk = nvec / kWave;
+    if (static_cast<int64_t>(S) * nchunk > 0x7FFFFFFFLL) return MOE_CEIL_ERR_ARG;
+    const dim3 grid(static_cast<unsigned>(groups)), block(kWave * waves_per_group);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const u32x4 *in = static_cast<const u32x4 *>(y);
+    u32x4 *o = static_cast<u32x4 *>(out);
+#define CEIL_GP(KK, KIND) hipLaunchKernelGGL((k_gather_persistent<KK, KIND>), grid, block, 0, s, in, nvec, rows, o, nchunk, S)
+    if (K == 8 && store_kind == STORE_SC1) CEIL_GP(8, STORE_SC1);
+    else if (K == 8 && store_kind == STORE_NT) CEIL_GP(8, STORE_NT);
+    else if (K == 8 && store_kind == STORE_PLAIN) CEIL_GP(8, STORE_PLAIN);
+    else if (K == 6 && store_kind == STORE_SC1) CEIL_GP(6, STORE_SC1);
+    else return MOE_CEIL_ERR_ARG;
+#undef CEIL_GP
     return launched();
 }

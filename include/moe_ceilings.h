@@ -67,6 +67,16 @@ int32_t moe_ceiling_scatter(const void *src, int32_t S, int32_t in_row_bytes, in
 int32_t moe_ceiling_gather(const void *y, int32_t S, int32_t row_bytes, int32_t K, const int32_t *rows,
                            int32_t vec_per_lane, int32_t store_kind, void *out, void *stream);
 
+/* The combine pattern in persistent form: `groups` workgroups of
+ * waves_per_group waves (1..4) walk the same (token, 1 KiB chunk) units as
+ * moe_ceiling_gather (chunk-fastest), each wave keeping the next unit's K row
+ * loads in flight while it combines and stores the current one.  Same
+ * output as moe_ceiling_gather with vec_per_lane 1.  K in {6, 8}; store_kind
+ * as in moe_ceiling_write (K = 6: SC1 only). */
+int32_t moe_ceiling_gather_persistent(const void *y, int32_t S, int32_t row_bytes, int32_t K, const int32_t *rows,
+                                      int32_t groups, int32_t waves_per_group, int32_t store_kind, void *out,
+                                      void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -179,7 +179,8 @@ def test_ceiling_library_exports_and_rejects_bad_arguments():
         __graft_entry__.build()
     text = re.sub(r"/\*.*?\*/", "", open(CEIL_HEADER).read(), flags=re.S)
     names = sorted(set(re.findall(r"\b(moe_ceiling_[a-z_0-9]+)\s*\(", text)))
-    assert names == ["moe_ceiling_gather", "moe_ceiling_read", "moe_ceiling_scatter", "moe_ceiling_write"]
+    assert names == ["moe_ceiling_gather", "moe_ceiling_gather_persistent", "moe_ceiling_read", "moe_ceiling_scatter",
+                     "moe_ceiling_write"]
     import bench
     L = bench.ceiling_lib()
     for n in names:
@@ -201,3 +202,14 @@ def test_ceiling_library_exports_and_rejects_bad_arguments():
     assert L.moe_ceiling_gather(P(A), 8, 3072, 8, P(A), 2, 0, P(A), None) == ERR         # 3 KiB in 2 KiB chunks
     assert L.moe_ceiling_gather(P(A), 0, 1024, 8, P(A), 1, 0, P(A), None) == ERR         # empty
     assert L.moe_ceiling_gather(P(A), 8, 1024, 8, None, 1, 0, P(A), None) == ERR         # no rows
+
+
+def test_ceiling_persistent_gather_rejects_bad_arguments():
+    import bench
+    L = bench.ceiling_lib()
+    P = ctypes.c_void_p
+    A = FAKE
+    assert L.moe_ceiling_gather_persistent(P(A), 8, 1024, 8, P(A), 0, 1, 2, P(A), None) == 1    # no groups
+    assert L.moe_ceiling_gather_persistent(P(A), 8, 1024, 8, P(A), 4, 5, 2, P(A), None) == 1    # 5 waves
+    assert L.moe_ceiling_gather_persistent(P(A), 8, 1024, 7, P(A), 4, 1, 2, P(A), None) == 1    # K = 7
+    assert L.moe_ceiling_gather_persistent(P(A), 8, 1536, 8, P(A), 4, 1, 2, P(A), None) == 1    # 1.5 KiB rows

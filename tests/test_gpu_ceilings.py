@@ -98,3 +98,29 @@ def test_gather(pat, v):
         pat.gather(y_d.view(torch.uint8), torch.from_numpy(rows).to(DEV), out.view(torch.uint8), v, kind)()
         torch.cuda.synchronize()
         assert np.array_equal(_u32(out), want), kind
+
+
+@pytest.mark.parametrize("groups,waves", [(1, 1), (3, 2), (2, 4), (64, 4)])
+def test_gather_persistent(pat, groups, waves):
+    """Same bytes as the gather pattern, whatever the number of persistent
+    waves (fewer waves than units, more waves than units)."""
+    print(f"case ceilings gather persistent groups={groups} waves={waves}", flush=True)
+    S, K, rb = 37, 8, 3072
+    rng = np.random.default_rng(5)
+    nrows = 300
+    y = rng.integers(0, 2 ** 32, (nrows, rb // 4), dtype=np.uint64).astype(np.uint32)
+    rows = rng.integers(0, nrows, (S, K)).astype(np.int32)
+    rows[3, 0] = -1
+    rows[36, 7] = -1
+    want = np.zeros((S, rb // 4), np.uint32)
+    for t in range(S):
+        for k in range(K):
+            if rows[t, k] >= 0:
+                want[t] ^= y[rows[t, k]]
+    y_d = torch.from_numpy(y.view(np.int32)).to(DEV)
+    for kind in ("plain", "sc1"):
+        out = torch.full((S, rb // 4), -1, dtype=torch.int32, device=DEV)
+        pat.gather_persistent(y_d.view(torch.uint8), torch.from_numpy(rows).to(DEV), out.view(torch.uint8),
+                              groups, waves, kind)()
+        torch.cuda.synchronize()
+        assert np.array_equal(_u32(out), want), kind
