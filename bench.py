@@ -368,11 +368,27 @@ def decode_numbers(moe, dcfg, dev, iters: int, drun=None):
     # a model's decode step captures every layer's calls in one graph: per
     # call inside a 64-call graph (64 MoE layers' dispatch + combine)
     g64_ms = time_graph(drun.fused_step, max(iters // 64, 4), 64)
+    # the fixed cost of one graph launch on this stack: a graph of two
+    # one-element fill kernels (the same node count as the decode call),
+    # replayed the same way, and the same two kernels launched eagerly
+    import torch
+    tiny = torch.zeros(1, dtype=torch.float32, device=dev)
+
+    def two_fills():
+        tiny.fill_(1.0)
+        tiny.fill_(2.0)
+
+    floor_ms = time_graph(two_fills, iters)
+    floor64_ms = time_graph(two_fills, max(iters // 64, 4), 64)
+    eager_fill_ms = time_calls(two_fills, iters)
     return {"us_per_call": round(fused_ms * 1e3, 2),
             "call": "moe_layout_dispatch (one launch) + moe_combine",
             "layout_dispatch_us": round(ld_ms * 1e3, 2), "combine_us": round(comb_ms * 1e3, 2),
             "graph_replay_us_per_call": round(g_ms * 1e3, 2),
             "graph_of_64_calls_us_per_call": round(g64_ms * 1e3, 2),
+            "two_fill_kernels": {"graph_replay_us": round(floor_ms * 1e3, 2),
+                                 "graph_of_64_us_per_pair": round(floor64_ms * 1e3, 2),
+                                 "eager_us_per_pair": round(eager_fill_ms * 1e3, 2)},
             "three_call_us_per_call": round(dt["step_ms"] * 1e3, 2),
             "config": {"workload": "decode", "S": dcfg.S, "H": dcfg.H, "E": dcfg.E, "K": dcfg.K,
                        "R": dcfg.R, "fp8": dcfg.fp8, "capacity": dcfg.pad_rows}}
