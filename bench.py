@@ -24,6 +24,8 @@ padded to 128 rows) is timed too.
   --ceilings         run only the pattern-ceiling kernels (libmoe_ceilings.so)
   --summarize DIR    turn a profiling run's rocprofv3 CSVs into markdown tables
                      and profiles/traffic.json (CPU only)
+  --ceilings-summary JSON
+                     profiles/ceilings.md from a saved --ceilings line (CPU only)
   --no-cpu-baseline  skip timing the CPU oracle
   --no-decode        skip the decode, balanced-layout and skewed-batch numbers
   --no-percentiles   skip the percentile pass and the streaming reference
@@ -503,7 +505,7 @@ def ceiling_lib():
     P, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
     L.moe_ceiling_read.argtypes = [P, i64, i32, i32, i32, P, P]
     L.moe_ceiling_write.argtypes = [P, i64, i32, i32, i32, P]
-    L.moe_ceiling_scatter.argtypes = [P, i32, i32, i32, P, P, i32, P, P]
+    L.moe_ceiling_scatter.argtypes = [P, i32, i32, i32, P, P, i32, P, i32, P]
     L.moe_ceiling_gather.argtypes = [P, i32, i32, i32, P, i32, i32, P, P]
     L.moe_ceiling_gather_persistent.argtypes = [P, i32, i32, i32, P, i32, i32, i32, P, P]
     for f in (L.moe_ceiling_read, L.moe_ceiling_write, L.moe_ceiling_scatter, L.moe_ceiling_gather,
@@ -553,13 +555,13 @@ class Patterns:
         return lambda: _checked(self.L.moe_ceiling_write(buf.data_ptr(), nb, v, w, STORE_KINDS[kind], self._s()),
                                 "write")
 
-    def scatter(self, src, rows, dst, scales=None):
+    def scatter(self, src, rows, dst, scales=None, waves=1):
         S, K = rows.shape
         in_rb = src.shape[1] * src.element_size()
         out_rb = dst.shape[1] * dst.element_size()
         sp = scales.data_ptr() if scales is not None else None
         return lambda: _checked(self.L.moe_ceiling_scatter(src.data_ptr(), S, in_rb, K, rows.data_ptr(),
-                                                           dst.data_ptr(), out_rb, sp, self._s()), "scatter")
+                                                           dst.data_ptr(), out_rb, sp, waves, self._s()), "scatter")
 
     def gather_persistent(self, y, rows, out, groups, waves, kind="sc1"):
         S, K = rows.shape
@@ -611,12 +613,15 @@ def ceiling_sweep(moe, dev, iters: int = 30):
     ms = time_calls(pat.scatter(src, rows, out8, sc8), iters, 5)
     res["scatter_fp8_rows"] = {"shape": f"S={S} K={K} H={H}: read 2 KiB, write 1 KiB x {K} + scales",
                                "bytes": b8, "gbps": _gbps(b8, ms)}
+    # FP8 rows hold 7 chunks at H = 7168, so multi-wave groups are timed on the bf16 rows (14 chunks)
     del out8, sc8
     out16 = torch.empty((S * K, 2 * H), dtype=torch.uint8, device=dev)
     b16 = S * 2 * H + S * K * 2 * H
     ms = time_calls(pat.scatter(src, rows, out16), iters, 5)
     res["scatter_bf16_rows"] = {"shape": f"S={S} K={K} H={H}: read 1 KiB, write 1 KiB x {K}",
                                 "bytes": b16, "gbps": _gbps(b16, ms)}
+    ms = time_calls(pat.scatter(src, rows, out16, None, 2), iters, 5)
+    res["scatter_bf16_rows"]["2 waves/group gbps"] = _gbps(b16, ms)
     y = out16
     out = torch.empty((S, 2 * H), dtype=torch.uint8, device=dev)
     bg = S * K * 2 * H + S * 2 * H
@@ -639,6 +644,76 @@ def ceiling_sweep(moe, dev, iters: int = 30):
     return res
 
 
+def ceilings_markdown(c: dict) -> str:
+    """profiles/ceilings.md from the JSON object that --ceilings prints."""
+    C = c["ceilings"]
+    R, W, G = C["read"], C["write"], C["gather"]
+    L = ["# Pattern ceilings — what HBM sustains for each access pattern (MI355X)\n",
+         "MI355X (gfx950), one GPU, ROCm 7.2.  Kernels: `combine_moe_layout_02_amd/csrc/ceilings.hip`",
+         "(`libmoe_ceilings.so`, header `include/moe_ceilings.h`): the dispatch and combine byte",
+         "patterns with no arithmetic.  HIP events on the launch stream, 30 back-to-back launches",
+         "after 5 warm-up launches, GB = 1e9.  Every launch in the first three sections moves at least",
+         "1 GiB, four times the 256 MB Infinity Cache.\n",
+         "Commands (repo root on the GPU box, then here):\n",
+         "    python3 bench.py --ceilings > gpurun_out/ceilings.json",
+         "    python3 bench.py --ceilings-summary gpurun_out/ceilings.json > profiles/ceilings.md\n",
+         "## Streaming read and write, 1 GiB\n",
+         "16-byte vectors; a wave covers V KiB contiguously (all its loads issued before any use);",
+         "W waves per workgroup.  NT = non-temporal; SC1 = buffer store with the SC1 cache-policy bit.\n",
+         "| shape | read plain | read NT | write plain | write NT | write SC1 |", "|---|---|---|---|---|---|"]
+    for v, w in ((1, 1), (4, 1), (16, 1), (1, 4), (4, 4), (16, 4)):
+        k = f"{v}KiB/wave x{w} waves"
+        g = lambda d, kind: f"{d[k + '/' + kind]:,.0f}" if k + "/" + kind in d else "—"
+        L.append(f"| {v} KiB/wave, {w} wave{'s' if w > 1 else ''}/group | {g(R, 'plain')} | {g(R, 'nt')} | "
+                 f"{g(W, 'plain')} | {g(W, 'nt')} | {g(W, 'sc1')} |")
+    sf, sb = C["scatter_fp8_rows"], C["scatter_bf16_rows"]
+    L += ["", "## Dispatch pattern (scatter), at >= 1 GiB\n",
+          "Each wave reads its chunk of one token row once and stores 1 KiB to each of the token's K",
+          "receive rows (NT stores); rows from a seeded uniform routing laid out by `moe_layout`.\n",
+          "| pattern | bytes per launch | single-wave groups GB/s | 2-wave groups GB/s |", "|---|---|---|---|",
+          f"| FP8 rows: {sf['shape']} | {sf['bytes']:,} | {sf['gbps']:,.0f} | — (7 chunks per row) |",
+          f"| bf16 rows: {sb['shape']} | {sb['bytes']:,} | {sb['gbps']:,.0f} | "
+          f"{sb.get('2 waves/group gbps', float('nan')):,.0f} |",
+          "", "## Combine pattern (gather), at >= 1 GiB\n",
+          f"{G['shape']}; NT gathers (all K of a unit issued before any use).\n",
+          "| form | output store plain | NT | SC1 |", "|---|---|---|---|"]
+    for v in (1, 2):
+        L.append(f"| single-wave workgroups, {v} KiB per wave | {G[f'{v}KiB/wave/plain']:,.0f} | "
+                 f"{G[f'{v}KiB/wave/nt']:,.0f} | {G[f'{v}KiB/wave/sc1']:,.0f} |")
+    L.append(f"| single-wave, 1 KiB, contiguous planes (row k*S+t, no routing) | — | — | "
+             f"{G['planes 1KiB/wave/sc1']:,.0f} |")
+    for key in sorted(k for k in G if k.startswith("persistent")):
+        per_cu, w = key.split()[1], key.split()[3].lstrip("x")
+        L.append(f"| persistent: {per_cu} workgroups per CU x {w} wave(s), next unit's rows in flight | — | — | "
+                 f"{G[key]:,.0f} |")
+    L += [f"\nBytes per launch: {G['bytes']:,}.  The persistent form walks the same units with a fixed grid;",
+          "each wave issues the next unit's K loads before it combines the current unit.\n",
+          "## Product kernels against their own pattern\n",
+          "The same command times each product kernel and the pattern kernel that moves its bytes with the",
+          "same rows (back-to-back launches of one kernel, the product's algorithmic bytes):\n",
+          "| workload | kernel | kernel µs | pattern µs | kernel GB/s | % of 8 TB/s | pattern GB/s | kernel / pattern |",
+          "|---|---|---|---|---|---|---|---|"]
+    for wl in ("prefill", "skew"):
+        for kn in ("dispatch", "combine"):
+            d = c[f"{wl}_vs_pattern"][kn]
+            L.append(f"| {wl} | {kn} | {d['kernel_us']} | {d['pattern_us']} | {d['kernel_gbps']:,.0f} | "
+                     f"{d['kernel_gbps'] / HBM_PEAK_GBPS * 100:.1f} | {d['pattern_gbps']:,.0f} | "
+                     f"{d['kernel_over_pattern']:.3f} |")
+    L.append("")
+    for wl in ("prefill", "skew"):
+        d = c[f"{wl}_vs_pattern"]
+        pers = d["combine"].get("persistent_pattern_us") or {}
+        if pers:
+            L.append(f"Persistent gather pattern at the {wl} shape (µs, same rows): "
+                     + ", ".join(f"{k} {v}" for k, v in pers.items())
+                     + f"; one single-wave workgroup per unit: {d['combine']['pattern_us']} µs.")
+        two = d["dispatch"].get("pattern_2_waves_per_group_us")
+        if two is not None:
+            L.append(f"Scatter pattern at the {wl} shape with 2-wave groups: {two} µs; single-wave groups: "
+                     f"{d['dispatch']['pattern_us']} µs.")
+    return "\n".join(L) + "\n"
+
+
 def pattern_vs_product(moe, run, dev, iters: int = 30):
     """The product dispatch and combine of this run next to the pattern kernels
     that move the same bytes with the same rows (no arithmetic), timed back to
@@ -656,6 +731,9 @@ def pattern_vs_product(moe, run, dev, iters: int = 30):
     gath = pat.gather(run.expert_out.view(torch.uint8), rows, run.buf.out.view(torch.uint8), 1, "sc1")
     t_d = time_calls(run.dispatch_call, iters, 5)
     t_sc = time_calls(scat, iters, 5)
+    t_sc2 = None
+    if (recv_u8.shape[1] // 1024) % 2 == 0:
+        t_sc2 = time_calls(pat.scatter(hid_u8, rows, recv_u8, run.buf.recv_scales, 2), iters, 5)
     t_c = time_calls(run.combine_call, iters, 5)
     t_g = time_calls(gath, iters, 5)
     n_cu = torch.cuda.get_device_properties(dev).multi_processor_count
@@ -670,7 +748,8 @@ def pattern_vs_product(moe, run, dev, iters: int = 30):
     out["dispatch"] = {"kernel_us": round(t_d * 1e3, 2), "pattern_us": round(t_sc * 1e3, 2),
                        "pattern": "moe_ceiling_scatter with the same rows and row bytes",
                        "kernel_gbps": _gbps(db, t_d), "pattern_gbps": _gbps(db, t_sc),
-                       "kernel_over_pattern": round(t_sc / t_d, 4)}
+                       "kernel_over_pattern": round(t_sc / t_d, 4),
+                       "pattern_2_waves_per_group_us": None if t_sc2 is None else round(t_sc2 * 1e3, 2)}
     out["combine"] = {"kernel_us": round(t_c * 1e3, 2), "pattern_us": round(t_g * 1e3, 2),
                       "pattern": "moe_ceiling_gather with the same rows, SC1 output store",
                       "kernel_gbps": _gbps(cb, t_c), "pattern_gbps": _gbps(cb, t_g),
@@ -910,6 +989,8 @@ def main(argv=None):
     ap.add_argument("--summarize", metavar="DIR",
                     help="summarize a profiling run's rocprofv3 CSVs (markdown to stdout) and write "
                          "profiles/traffic.json; runs on the CPU")
+    ap.add_argument("--ceilings-summary", metavar="JSON",
+                    help="print profiles/ceilings.md from the JSON object --ceilings printed (CPU only)")
     ap.add_argument("--ceilings", action="store_true",
                     help="time only the pattern-ceiling kernels (>= 1 GiB per launch) and the prefill "
                          "dispatch / combine against their own patterns; print one JSON object")
@@ -931,6 +1012,10 @@ def main(argv=None):
         return
     if args.summarize:
         print(summarize_profiles(args.summarize))
+        return
+    if args.ceilings_summary:
+        with open(args.ceilings_summary) as f:
+            print(ceilings_markdown(json.loads(f.read().strip().splitlines()[-1])), end="")
         return
 
     import torch

@@ -86,12 +86,17 @@ __global__ void k_write(u32x4 *__restrict__ dst, unsigned int magic) {
 
 // IN = 1: a bf16 row chunk goes out as it came in; IN = 2: two input vectors
 // make one output vector (the FP8 dispatch's 2:1 byte ratio).
+// A workgroup of W waves covers W consecutive 1 KiB chunks of one token's
+// output rows (W = 1: the product dispatch kernels' shape).
 template <int K, int IN>
-__global__ __launch_bounds__(kWave) void k_scatter(const u32x4 *__restrict__ src, int out_nvec,
-                                                   const int32_t *__restrict__ rows, u32x4 *__restrict__ dst,
-                                                   float *__restrict__ scales, int nchunk) {
-    const int t = blockIdx.x / nchunk, c = blockIdx.x % nchunk;
-    const int v = c * kWave + threadIdx.x;
+__global__ __launch_bounds__(256) void k_scatter(const u32x4 *__restrict__ src, int out_nvec,
+                                                 const int32_t *__restrict__ rows, u32x4 *__restrict__ dst,
+                                                 float *__restrict__ scales, int nchunk) {
+    const int W = blockDim.x / kWave;
+    const int groups_per_token = nchunk / W;
+    const int t = blockIdx.x / groups_per_token;
+    const int c = (blockIdx.x % groups_per_token) * W + static_cast<int>(threadIdx.x / kWave);
+    const int v = c * kWave + static_cast<int>(threadIdx.x % kWave);
     const int32_t *pr = rows + static_cast<size_t>(t) * K;
     int p[K];
 #pragma unroll
@@ -104,7 +109,7 @@ __global__ __launch_bounds__(kWave) void k_scatter(const u32x4 *__restrict__ src
     for (int k = 0; k < K; ++k) {
         if (p[k] >= 0) {
             __builtin_nontemporal_store(x, dst + static_cast<size_t>(p[k]) * out_nvec + v);
-            if (scales != nullptr && (threadIdx.x & 7) == 0)
+            if (scales != nullptr && (v & 7) == 0)
                 scales[static_cast<size_t>(p[k]) * (out_nvec / 8) + v / 8] = __uint_as_float(x[0] & 0x3F7FFFFFu);
         }
     }
@@ -305,13 +310,14 @@ extern "C" int32_t moe_ceiling_write(void *dst, int64_t bytes, int32_t vec_per_l
 
 extern "C" int32_t moe_ceiling_scatter(const void *src, int32_t S, int32_t in_row_bytes, int32_t K,
                                        const int32_t *rows, void *dst, int32_t out_row_bytes, float *scales,
-                                       void *stream) {
+                                       int32_t waves_per_group, void *stream) {
     if (src == nullptr || rows == nullptr || dst == nullptr || !aligned16(src) || !aligned16(dst)) return MOE_CEIL_ERR_ARG;
     if (S < 1 || out_row_bytes < 1024 || out_row_bytes % 1024) return MOE_CEIL_ERR_ARG;
     if (in_row_bytes != out_row_bytes && in_row_bytes != 2 * out_row_bytes) return MOE_CEIL_ERR_ARG;
     const int out_nvec = out_row_bytes / 16, nchunk = out_nvec / kWave;
+    if (waves_per_group < 1 || waves_per_group > 4 || nchunk % waves_per_group) return MOE_CEIL_ERR_ARG;
     if (static_cast<int64_t>(S) * nchunk > 0x7FFFFFFFLL) return MOE_CEIL_ERR_ARG;
-    const dim3 grid(static_cast<unsigned>(S * nchunk)), block(kWave);
+    const dim3 grid(static_cast<unsigned>(S * (nchunk / waves_per_group))), block(kWave * waves_per_group);
     hipStream_t s = static_cast<hipStream_t>(stream);
     const u32x4 *in = static_cast<const u32x4 *>(src);
     u32x4 *out = static_cast<u32x4 *>(dst);

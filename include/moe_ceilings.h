@@ -46,16 +46,18 @@ int32_t moe_ceiling_write(void *dst, int64_t bytes, int32_t vec_per_lane, int32_
                           int32_t store_kind, void *stream);
 
 /* The dispatch pattern: for each token t < S and each 1 KiB chunk of an output
- * row, one single-wave workgroup reads the matching in_row_bytes/out_row_bytes
- * KiB of src row t ([S, in_row_bytes]) and stores 1 KiB to dst row rows[t*K+k]
+ * row, one wave reads the matching in_row_bytes/out_row_bytes KiB of src row t
+ * ([S, in_row_bytes]) and stores 1 KiB to dst row rows[t*K+k]
  * ([*, out_row_bytes]) for every k with rows[t*K+k] >= 0 (non-temporal
  * stores).  With `scales` ([*, out_row_bytes/128] fp32, or NULL) one lane in 8
  * also stores a 4-byte value per 128 output bytes, as FP8 dispatch does.
+ * A workgroup holds waves_per_group (1..4, dividing the chunks per row)
+ * waves on consecutive chunks of one token (1: the dispatch kernels' shape).
  * in_row_bytes is out_row_bytes (bf16 dispatch) or twice it (FP8 dispatch);
  * out_row_bytes is a multiple of 1024; K in {1,2,4,6,8}.  Every rows entry
  * must be -1 or a row of dst. */
 int32_t moe_ceiling_scatter(const void *src, int32_t S, int32_t in_row_bytes, int32_t K, const int32_t *rows,
-                            void *dst, int32_t out_row_bytes, float *scales, void *stream);
+                            void *dst, int32_t out_row_bytes, float *scales, int32_t waves_per_group, void *stream);
 
 /* The combine pattern: for each token t < S and each vec_per_lane KiB chunk of
  * a row, one single-wave workgroup issues non-temporal loads of that chunk of

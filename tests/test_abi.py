@@ -196,9 +196,11 @@ def test_ceiling_library_exports_and_rejects_bad_arguments():
     assert L.moe_ceiling_read(P(A), 3 << 10, 1, 2, 0, P(A), None) == ERR              # 3 KiB over 2-wave groups
     assert L.moe_ceiling_write(P(A), 1 << 20, 1, 17, 0, None) == ERR                  # too many waves
     assert L.moe_ceiling_write(P(A), 1 << 20, 1, 1, 3, None) == ERR                   # unknown store kind
-    assert L.moe_ceiling_scatter(P(A), 8, 3000, 8, P(A), P(A), 1024, None, None) == ERR   # row ratio
-    assert L.moe_ceiling_scatter(P(A), 8, 1536, 8, P(A), P(A), 1536, None, None) == ERR   # not whole KiB
-    assert L.moe_ceiling_scatter(P(A), 8, 2048, 3, P(A), P(A), 1024, None, None) == ERR   # K = 3
+    assert L.moe_ceiling_scatter(P(A), 8, 3000, 8, P(A), P(A), 1024, None, 1, None) == ERR   # row ratio
+    assert L.moe_ceiling_scatter(P(A), 8, 1536, 8, P(A), P(A), 1536, None, 1, None) == ERR   # not whole KiB
+    assert L.moe_ceiling_scatter(P(A), 8, 2048, 3, P(A), P(A), 1024, None, 1, None) == ERR   # K = 3
+    assert L.moe_ceiling_scatter(P(A), 8, 6144, 8, P(A), P(A), 3072, None, 2, None) == ERR   # 3 chunks in pairs
+    assert L.moe_ceiling_scatter(P(A), 8, 4096, 8, P(A), P(A), 4096, None, 5, None) == ERR   # 5 waves
     assert L.moe_ceiling_gather(P(A), 8, 3072, 8, P(A), 2, 0, P(A), None) == ERR         # 3 KiB in 2 KiB chunks
     assert L.moe_ceiling_gather(P(A), 0, 1024, 8, P(A), 1, 0, P(A), None) == ERR         # empty
     assert L.moe_ceiling_gather(P(A), 8, 1024, 8, None, 1, 0, P(A), None) == ERR         # no rows

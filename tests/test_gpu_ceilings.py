@@ -45,10 +45,10 @@ def test_read_write(pat, v, w):
         assert np.array_equal(_u32(out).reshape(nvec, 4), want), kind
 
 
-@pytest.mark.parametrize("fp8", [False, True])
-def test_scatter(pat, fp8):
-    print(f"case ceilings scatter fp8={fp8}", flush=True)
-    S, K, out_rb = 6, 4, 2048
+@pytest.mark.parametrize("fp8,waves", [(False, 1), (True, 1), (False, 2), (True, 4)])
+def test_scatter(pat, fp8, waves):
+    print(f"case ceilings scatter fp8={fp8} waves={waves}", flush=True)
+    S, K, out_rb = 6, 4, 4096
     in_rb = 2 * out_rb if fp8 else out_rb
     rng = np.random.default_rng(3)
     src = rng.integers(0, 2 ** 32, (S, in_rb // 4), dtype=np.uint64).astype(np.uint32)
@@ -59,7 +59,7 @@ def test_scatter(pat, fp8):
     dst = torch.full((nrows, out_rb // 4), -1, dtype=torch.int32, device=DEV)
     sc = torch.full((nrows, out_rb // 128), -1, dtype=torch.int32, device=DEV) if fp8 else None
     pat.scatter(src_d.view(torch.uint8), torch.from_numpy(rows).to(DEV), dst.view(torch.uint8),
-                sc.view(torch.float32) if fp8 else None)()
+                sc.view(torch.float32) if fp8 else None, waves)()
     torch.cuda.synchronize()
     got = _u32(dst)
     vec = src.reshape(S, -1, 2, 4)
