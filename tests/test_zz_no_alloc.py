@@ -66,3 +66,51 @@ def test_noalloc_rejects_what_does_not_fit():
     b = moe.moe_layout_bufs(*([1 << 20] * 7))
     assert lib.moe_layout_noalloc(ctypes.byref(d), ctypes.c_void_p(1 << 20), ctypes.byref(b), None) == \
         moe.MOE_ERR_WORKSPACE
+
+
+def test_noalloc_under_graph_capture():
+    """The allocation-free layout captured in a HIP graph (code under graph
+    capture is a caller it exists for) and replayed with new routing written
+    into the captured input between replays: every replay equals moe_layout
+    (caller workspace, eager) on that routing, and the first also the oracle."""
+    import combine_moe_layout_02_amd as moe
+    S, K, E, R = 16384, 6, 64, 8                       # two-launch form: uses the library's scratch
+    desc = moe.LayoutDesc(S, K, E, R)
+    rng = np.random.default_rng(9300)
+
+    def routing(bad: bool):
+        p = rng.random(E) ** 2
+        idx = rng.choice(E, size=(S, K), p=p / p.sum()).astype(np.int32)
+        if bad:
+            idx.reshape(-1)[rng.integers(0, idx.size, 11)] = -3
+        return idx
+
+    idx_d = torch.from_numpy(routing(False)).to(DEV)
+    got = moe.alloc_layout(desc, DEV)
+    got.workspace = None
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        moe.moe_layout_noalloc(desc, idx_d, got)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        moe.moe_layout_noalloc(desc, idx_d, got)
+    torch.cuda.synchronize()
+    fields = ("tokens_per_expert", "tokens_per_rank", "expert_offset", "rank_offset", "pos", "src", "status")
+    for rep in range(4):
+        print(f"case noalloc graph replay {rep}", flush=True)
+        idx = routing(bad=rep == 2)
+        idx_d.copy_(torch.from_numpy(idx))
+        for f in fields:
+            getattr(got, f).fill_(-7)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        want = moe.moe_layout(desc, idx_d)
+        torch.cuda.synchronize()
+        for f in fields:
+            assert torch.equal(getattr(got, f), getattr(want, f)), f"replay {rep}: {f}"
+        if rep == 0:
+            compare_layout(got, oracle.layout(idx, E, R), "noalloc graph replay")
