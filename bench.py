@@ -1080,6 +1080,9 @@ def main(argv=None):
         extra.update(cold_dc(pct["batch"], db + cb))
         if also is not None:
             also.update(cold_dc(pct["skew"], also["bytes"]["dispatch"] + also["bytes"]["combine"]))
+            # the same-shape skewed batch's cold figures beside the batch's own
+            extra.update({f"skew_{k}": v for k, v in cold_dc(pct["skew"], also["bytes"]["dispatch"] +
+                                                               also["bytes"]["combine"]).items()})
     del srun
     balanced = None if args.no_decode else balanced_numbers(moe, CONFIGS["skew"], dev)
     budgets = [int(x) for x in args.cu_budgets.split(",") if x.strip()]
