@@ -759,7 +759,7 @@ def pattern_vs_product(moe, run, dev, iters: int = 30):
 
 
 def cpu_baseline(cfg, budget_s: float = 12.0):
-    """The CPU oracle (single-threaded C) on the same workload: layout, dispatch
+    """The CPU oracle (single-threaded C++) on the same workload: layout, dispatch
     and combine of full batches, repeated until ~budget_s of work."""
     import numpy as np
     import oracle

@@ -1,7 +1,8 @@
 """CPU oracle for MoE expert-parallel layout, dispatch and combine (ctypes front end).
 
-TEST INFRASTRUCTURE ONLY.  The oracle is a plain, single-threaded C library
-(``moe_oracle.c``) that shares no code with the GPU library.  Only the test
+TEST INFRASTRUCTURE ONLY.  The oracle is a plain, single-threaded C++ library
+(``moe_oracle.cpp``, the plain C subset of C++) that shares no code with the
+GPU library.  Only the test
 suite, the smoke check and the benchmark's CPU-baseline leg may import this
 package; the GPU path never calls it and never falls back to it.
 
@@ -18,7 +19,7 @@ from typing import Optional
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-SRC = os.path.join(_HERE, "moe_oracle.c")
+SRC = os.path.join(_HERE, "moe_oracle.cpp")
 LIB = os.path.join(_HERE, "libmoe_oracle.so")
 
 PAD_NONE, PAD_MULTIPLE, PAD_CAPACITY = 0, 1, 2
@@ -27,9 +28,9 @@ OK, ERR_NULL, ERR_SHAPE = 0, 1, 2
 
 
 def build() -> str:
-    """Compile the oracle with gcc (IEEE fp32, no contraction)."""
+    """Compile the oracle with g++ (IEEE fp32, no contraction)."""
     tmp = LIB + ".tmp"
-    subprocess.run(["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math",
+    subprocess.run(["g++", "-O2", "-std=c++17", "-ffp-contract=off", "-fno-fast-math",
                     "-Wall", "-Wextra", "-shared", "-fPIC", "-o", tmp, SRC, "-lm"],
                    check=True)
     os.replace(tmp, LIB)
@@ -179,7 +180,7 @@ class BalancedLayout(Layout):
 
 
 def layout_balanced(topk_idx: np.ndarray, E: int, R: int, B: int) -> BalancedLayout:
-    """Balanced layout with B redundant-expert slots per rank (see moe_oracle.c)."""
+    """Balanced layout with B redundant-expert slots per rank (see moe_oracle.cpp)."""
     idx = _c(topk_idx, np.int32)
     S, K = idx.shape
     if max_recv_rows(S, K, E, R) < 0 or not 0 <= B <= 64:

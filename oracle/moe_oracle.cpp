@@ -1,5 +1,5 @@
 /*
- * moe_oracle.c -- plain, slow, single-threaded CPU oracle for MoE expert-parallel
+ * moe_oracle.cpp -- plain, slow, single-threaded CPU oracle for MoE expert-parallel
  * layout, dispatch and combine.
  *
  * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
@@ -7,9 +7,11 @@
  * code, header, table or constant generator with the GPU library: every
  * routine here is written out from the definition of the operation.
  *
- * Build: gcc -O2 -std=c11 -ffp-contract=off -fno-fast-math -shared -fPIC
+ * Build: g++ -O2 -std=c++17 -ffp-contract=off -fno-fast-math -shared -fPIC
  *        (IEEE fp32 with no contraction: every fused multiply-add below is an
- *        explicit fmaf call).
+ *        explicit fmaf call).  Written in the plain C subset of C++: loops,
+ *        arrays and the C math library, nothing that hides a step; every
+ *        exported function has C linkage (extern "C") for the test harnesses.
  *
  * What is computed, and the passage each step follows:
  *   - Expert parallelism spreads the experts of one MoE layer over the ranks of
@@ -43,6 +45,8 @@
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
+
+extern "C" {
 
 enum { OR_OK = 0, OR_ERR_NULL = 1, OR_ERR_SHAPE = 2 };
 enum { OR_PAD_NONE = 0, OR_PAD_MULTIPLE = 1, OR_PAD_CAPACITY = 2 };
@@ -498,3 +502,5 @@ planned:;
     free(home); free(order); free(seg); free(seen);
     return OR_OK;
 }
+
+}  // extern "C"

@@ -15,7 +15,7 @@ def pytest_configure(config):
 @pytest.fixture(scope="session", autouse=True)
 def _oracle_built():
     """The oracle is compiled by __graft_entry__.build(); build it only when
-    nothing is built yet (gcc takes about a second)."""
+    nothing is built yet (g++ takes about a second)."""
     import oracle
     if not os.path.exists(oracle.LIB):
         oracle.build()

@@ -1,7 +1,8 @@
 /* Memory and undefined-behaviour check of the CPU oracle (test infrastructure).
  *
- * Built by tests/test_oracle_sanitize.py with gcc -fsanitize=address,undefined
- * together with oracle/moe_oracle.c, and run on the host.  Every output buffer
+ * Built by tests/test_oracle_sanitize.py with -fsanitize=address,undefined
+ * and linked with oracle/moe_oracle.cpp (whose functions have C linkage), and
+ * run on the host.  Every output buffer
  * is allocated at exactly the size the oracle's header comments state, so an
  * access one element past it stops the program; each call's results are also
  * checked against the invariants that hold for any input (every valid entry
