@@ -508,8 +508,9 @@ def ceiling_lib():
     L.moe_ceiling_scatter.argtypes = [P, i32, i32, i32, P, P, i32, P, i32, P]
     L.moe_ceiling_gather.argtypes = [P, i32, i32, i32, P, i32, i32, P, P]
     L.moe_ceiling_gather_persistent.argtypes = [P, i32, i32, i32, P, i32, i32, i32, P, P]
+    L.moe_ceiling_scatter_rows.argtypes = [P, i32, i32, i32, P, P, i32, P, P]
     for f in (L.moe_ceiling_read, L.moe_ceiling_write, L.moe_ceiling_scatter, L.moe_ceiling_gather,
-              L.moe_ceiling_gather_persistent):
+              L.moe_ceiling_gather_persistent, L.moe_ceiling_scatter_rows):
         f.restype = i32
     return L
 
@@ -563,6 +564,14 @@ class Patterns:
         return lambda: _checked(self.L.moe_ceiling_scatter(src.data_ptr(), S, in_rb, K, rows.data_ptr(),
                                                            dst.data_ptr(), out_rb, sp, waves, self._s()), "scatter")
 
+    def scatter_rows(self, src, rows, dst, scales=None):
+        S, K = rows.shape
+        in_rb = src.shape[1] * src.element_size()
+        out_rb = dst.shape[1] * dst.element_size()
+        sp = scales.data_ptr() if scales is not None else None
+        return lambda: _checked(self.L.moe_ceiling_scatter_rows(src.data_ptr(), S, in_rb, K, rows.data_ptr(),
+                                                                dst.data_ptr(), out_rb, sp, self._s()), "scatter_rows")
+
     def gather_persistent(self, y, rows, out, groups, waves, kind="sc1"):
         S, K = rows.shape
         rb = y.shape[1] * y.element_size()
@@ -613,6 +622,8 @@ def ceiling_sweep(moe, dev, iters: int = 30):
     ms = time_calls(pat.scatter(src, rows, out8, sc8), iters, 5)
     res["scatter_fp8_rows"] = {"shape": f"S={S} K={K} H={H}: read 2 KiB, write 1 KiB x {K} + scales",
                                "bytes": b8, "gbps": _gbps(b8, ms)}
+    ms = time_calls(pat.scatter_rows(src, rows, out8, sc8), iters, 5)
+    res["scatter_fp8_rows"]["row order gbps"] = _gbps(b8, ms)
     # FP8 rows hold 7 chunks at H = 7168, so multi-wave groups are timed on the bf16 rows (14 chunks)
     del out8, sc8
     out16 = torch.empty((S * K, 2 * H), dtype=torch.uint8, device=dev)
@@ -622,6 +633,8 @@ def ceiling_sweep(moe, dev, iters: int = 30):
                                 "bytes": b16, "gbps": _gbps(b16, ms)}
     ms = time_calls(pat.scatter(src, rows, out16, None, 2), iters, 5)
     res["scatter_bf16_rows"]["2 waves/group gbps"] = _gbps(b16, ms)
+    ms = time_calls(pat.scatter_rows(src, rows, out16), iters, 5)
+    res["scatter_bf16_rows"]["row order gbps"] = _gbps(b16, ms)
     y = out16
     out = torch.empty((S, 2 * H), dtype=torch.uint8, device=dev)
     bg = S * K * 2 * H + S * 2 * H
@@ -670,10 +683,15 @@ def ceilings_markdown(c: dict) -> str:
     L += ["", "## Dispatch pattern (scatter), at >= 1 GiB\n",
           "Each wave reads its chunk of one token row once and stores 1 KiB to each of the token's K",
           "receive rows (NT stores); rows from a seeded uniform routing laid out by `moe_layout`.\n",
-          "| pattern | bytes per launch | single-wave groups GB/s | 2-wave groups GB/s |", "|---|---|---|---|",
-          f"| FP8 rows: {sf['shape']} | {sf['bytes']:,} | {sf['gbps']:,.0f} | — (7 chunks per row) |",
+          "| pattern | bytes per launch | single-wave groups GB/s | 2-wave groups GB/s | row order GB/s |",
+          "|---|---|---|---|---|",
+          f"| FP8 rows: {sf['shape']} | {sf['bytes']:,} | {sf['gbps']:,.0f} | — (7 chunks per row) | "
+          f"{sf.get('row order gbps', float('nan')):,.0f} |",
           f"| bf16 rows: {sb['shape']} | {sb['bytes']:,} | {sb['gbps']:,.0f} | "
-          f"{sb.get('2 waves/group gbps', float('nan')):,.0f} |",
+          f"{sb.get('2 waves/group gbps', float('nan')):,.0f} | {sb.get('row order gbps', float('nan')):,.0f} |",
+          "",
+          "Row order: one workgroup of K waves per token loads the row into LDS (each wave 1/K), then",
+          "wave k stores the whole output row contiguously to its receive row.",
           "", "## Combine pattern (gather), at >= 1 GiB\n",
           f"{G['shape']}; NT gathers (all K of a unit issued before any use).\n",
           "| form | output store plain | NT | SC1 |", "|---|---|---|---|"]
@@ -707,6 +725,10 @@ def ceilings_markdown(c: dict) -> str:
             L.append(f"Persistent gather pattern at the {wl} shape (µs, same rows): "
                      + ", ".join(f"{k} {v}" for k, v in pers.items())
                      + f"; one single-wave workgroup per unit: {d['combine']['pattern_us']} µs.")
+        ro = d["dispatch"].get("pattern_row_order_us")
+        if ro is not None:
+            L.append(f"Scatter pattern at the {wl} shape in row order (a workgroup per token through LDS): {ro} µs; "
+                     f"one wave per 1 KiB chunk: {d['dispatch']['pattern_us']} µs.")
         two = d["dispatch"].get("pattern_2_waves_per_group_us")
         if two is not None:
             L.append(f"Scatter pattern at the {wl} shape with 2-wave groups: {two} µs; single-wave groups: "
@@ -734,6 +756,7 @@ def pattern_vs_product(moe, run, dev, iters: int = 30):
     t_sc2 = None
     if (recv_u8.shape[1] // 1024) % 2 == 0:
         t_sc2 = time_calls(pat.scatter(hid_u8, rows, recv_u8, run.buf.recv_scales, 2), iters, 5)
+    t_rows = time_calls(pat.scatter_rows(hid_u8, rows, recv_u8, run.buf.recv_scales), iters, 5)
     t_c = time_calls(run.combine_call, iters, 5)
     t_g = time_calls(gath, iters, 5)
     n_cu = torch.cuda.get_device_properties(dev).multi_processor_count
@@ -749,7 +772,8 @@ def pattern_vs_product(moe, run, dev, iters: int = 30):
                        "pattern": "moe_ceiling_scatter with the same rows and row bytes",
                        "kernel_gbps": _gbps(db, t_d), "pattern_gbps": _gbps(db, t_sc),
                        "kernel_over_pattern": round(t_sc / t_d, 4),
-                       "pattern_2_waves_per_group_us": None if t_sc2 is None else round(t_sc2 * 1e3, 2)}
+                       "pattern_2_waves_per_group_us": None if t_sc2 is None else round(t_sc2 * 1e3, 2),
+                       "pattern_row_order_us": round(t_rows * 1e3, 2)}
     out["combine"] = {"kernel_us": round(t_c * 1e3, 2), "pattern_us": round(t_g * 1e3, 2),
                       "pattern": "moe_ceiling_gather with the same rows, SC1 output store",
                       "kernel_gbps": _gbps(cb, t_c), "pattern_gbps": _gbps(cb, t_g),

@@ -115,6 +115,36 @@ __global__ __launch_bounds__(256) void k_scatter(const u32x4 *__restrict__ src, 
     }
 }
 
+// The dispatch bytes in row order through LDS: one workgroup of K waves per
+// token; the waves load the token row into LDS together (each wave 1/K of
+// it), then wave k stores the whole output row, contiguously, to row
+// rows[t*K+k] (NT stores; with `scales`, one lane in 8 stores a 4-byte value
+// per 128 output bytes).  IN = 2: two input vectors make one output vector.
+template <int K, int IN>
+__global__ __launch_bounds__(512) void k_scatter_rows(const u32x4 *__restrict__ src, int out_nvec,
+                                                      const int32_t *__restrict__ rows, u32x4 *__restrict__ dst,
+                                                      float *__restrict__ scales) {
+    extern __shared__ u32x4 s_row[];   // [out_nvec] output vectors of the token
+    const int t = blockIdx.x;
+    const int w = static_cast<int>(threadIdx.x / kWave), lane = static_cast<int>(threadIdx.x % kWave);
+    const u32x4 *s = src + static_cast<size_t>(t) * out_nvec * IN;
+    for (int j = static_cast<int>(threadIdx.x); j < out_nvec; j += K * kWave) {
+        u32x4 x = s[static_cast<size_t>(j) * IN];
+        if constexpr (IN == 2) x ^= s[static_cast<size_t>(j) * IN + 1];
+        s_row[j] = x;
+    }
+    __syncthreads();
+    const int p = rows[static_cast<size_t>(t) * K + w];
+    if (p < 0) return;
+    u32x4 *drow = dst + static_cast<size_t>(p) * out_nvec;
+    for (int j = lane; j < out_nvec; j += kWave) {
+        const u32x4 x = s_row[j];
+        __builtin_nontemporal_store(x, drow + j);
+        if (scales != nullptr && (j & 7) == 0)
+            scales[static_cast<size_t>(p) * (out_nvec / 8) + j / 8] = __uint_as_float(x[0] & 0x3F7FFFFFu);
+    }
+}
+
 template <int K, int V, int KIND>
 __global__ __launch_bounds__(kWave) void k_gather(const u32x4 *__restrict__ y, int nvec,
                                                   const int32_t *__restrict__ rows, u32x4 *__restrict__ out,
@@ -385,5 +415,34 @@ extern "C" int32_t moe_ceiling_gather_persistent(const void *y, int32_t S, int32
     else if (K == 6 && store_kind == STORE_SC1) CEIL_GP(6, STORE_SC1);
     else return MOE_CEIL_ERR_ARG;
 #undef CEIL_GP
+    return launched();
+}
+
+extern "C" int32_t moe_ceiling_scatter_rows(const void *src, int32_t S, int32_t in_row_bytes, int32_t K,
+                                            const int32_t *rows, void *dst, int32_t out_row_bytes, float *scales,
+                                            void *stream) {
+    if (src == nullptr || rows == nullptr || dst == nullptr || !aligned16(src) || !aligned16(dst)) return MOE_CEIL_ERR_ARG;
+    if (S < 1 || out_row_bytes < 1024 || out_row_bytes % 1024 || out_row_bytes > 64 * 1024) return MOE_CEIL_ERR_ARG;
+    if (in_row_bytes != out_row_bytes && in_row_bytes != 2 * out_row_bytes) return MOE_CEIL_ERR_ARG;
+    const int out_nvec = out_row_bytes / 16;
+    const dim3 grid(static_cast<unsigned>(S));
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const u32x4 *in = static_cast<const u32x4 *>(src);
+    u32x4 *out = static_cast<u32x4 *>(dst);
+    const size_t lds = static_cast<size_t>(out_row_bytes);
+#define CEIL_SR(KK)                                                                                                \
+    {                                                                                                              \
+        const dim3 block(kWave * KK);                                                                              \
+        if (in_row_bytes == out_row_bytes)                                                                         \
+            hipLaunchKernelGGL((k_scatter_rows<KK, 1>), grid, block, lds, s, in, out_nvec, rows, out, scales);    \
+        else                                                                                                       \
+            hipLaunchKernelGGL((k_scatter_rows<KK, 2>), grid, block, lds, s, in, out_nvec, rows, out, scales);    \
+    }
+    switch (K) {
+        case 6: CEIL_SR(6) break;
+        case 8: CEIL_SR(8) break;
+        default: return MOE_CEIL_ERR_ARG;
+    }
+#undef CEIL_SR
     return launched();
 }

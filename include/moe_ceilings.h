@@ -69,6 +69,16 @@ int32_t moe_ceiling_scatter(const void *src, int32_t S, int32_t in_row_bytes, in
 int32_t moe_ceiling_gather(const void *y, int32_t S, int32_t row_bytes, int32_t K, const int32_t *rows,
                            int32_t vec_per_lane, int32_t store_kind, void *out, void *stream);
 
+/* The dispatch bytes in row order through LDS: one workgroup of K waves per
+ * token loads the token row (src row t) into LDS, each wave a 1/K share, then
+ * wave k stores the whole out_row_bytes row contiguously to dst row
+ * rows[t*K+k] (non-temporal), plus the 4-byte values per 128 output bytes
+ * into `scales` when given, as moe_ceiling_scatter does.  Same output as
+ * moe_ceiling_scatter.  K in {6, 8}; out_row_bytes a multiple of 1024, at
+ * most 64 KiB (the LDS row); in_row_bytes as in moe_ceiling_scatter. */
+int32_t moe_ceiling_scatter_rows(const void *src, int32_t S, int32_t in_row_bytes, int32_t K, const int32_t *rows,
+                                 void *dst, int32_t out_row_bytes, float *scales, void *stream);
+
 /* The combine pattern in persistent form: `groups` workgroups of
  * waves_per_group waves (1..4) walk the same (token, 1 KiB chunk) units as
  * moe_ceiling_gather (chunk-fastest), each wave keeping the next unit's K row

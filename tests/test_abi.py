@@ -180,7 +180,7 @@ def test_ceiling_library_exports_and_rejects_bad_arguments():
     text = re.sub(r"/\*.*?\*/", "", open(CEIL_HEADER).read(), flags=re.S)
     names = sorted(set(re.findall(r"\b(moe_ceiling_[a-z_0-9]+)\s*\(", text)))
     assert names == ["moe_ceiling_gather", "moe_ceiling_gather_persistent", "moe_ceiling_read", "moe_ceiling_scatter",
-                     "moe_ceiling_write"]
+                     "moe_ceiling_scatter_rows", "moe_ceiling_write"]
     import bench
     L = bench.ceiling_lib()
     for n in names:
@@ -215,3 +215,13 @@ def test_ceiling_persistent_gather_rejects_bad_arguments():
     assert L.moe_ceiling_gather_persistent(P(A), 8, 1024, 8, P(A), 4, 5, 2, P(A), None) == 1    # 5 waves
     assert L.moe_ceiling_gather_persistent(P(A), 8, 1024, 7, P(A), 4, 1, 2, P(A), None) == 1    # K = 7
     assert L.moe_ceiling_gather_persistent(P(A), 8, 1536, 8, P(A), 4, 1, 2, P(A), None) == 1    # 1.5 KiB rows
+
+
+def test_ceiling_scatter_rows_rejects_bad_arguments():
+    import bench
+    L = bench.ceiling_lib()
+    P = ctypes.c_void_p
+    A = FAKE
+    assert L.moe_ceiling_scatter_rows(P(A), 8, 2048, 7, P(A), P(A), 1024, None, None) == 1       # K = 7
+    assert L.moe_ceiling_scatter_rows(P(A), 8, 3072, 8, P(A), P(A), 1024, None, None) == 1       # row ratio
+    assert L.moe_ceiling_scatter_rows(P(A), 8, 131072, 8, P(A), P(A), 131072, None, None) == 1   # row > 64 KiB

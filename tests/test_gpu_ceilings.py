@@ -78,6 +78,36 @@ def test_scatter(pat, fp8, waves):
     assert np.all(got[~written] == 0xFFFFFFFF)
 
 
+@pytest.mark.parametrize("fp8", [False, True])
+def test_scatter_rows_matches_scatter(pat, fp8):
+    """Row order through LDS writes the same bytes as the chunked scatter."""
+    print(f"case ceilings scatter rows fp8={fp8}", flush=True)
+    S, K, out_rb = 5, 8, 3072
+    in_rb = 2 * out_rb if fp8 else out_rb
+    rng = np.random.default_rng(6)
+    src = rng.integers(0, 2 ** 32, (S, in_rb // 4), dtype=np.uint64).astype(np.uint32)
+    nrows = S * K + 3
+    rows = rng.permutation(nrows)[:S * K].astype(np.int32).reshape(S, K)
+    rows[1, 5] = -1
+    src_d = torch.from_numpy(src.view(np.int32)).to(DEV).view(torch.uint8)
+    rows_d = torch.from_numpy(rows).to(DEV)
+    outs = []
+    for form in ("chunks", "rows"):
+        dst = torch.full((nrows, out_rb // 4), -1, dtype=torch.int32, device=DEV)
+        sc = torch.full((nrows, out_rb // 128), -1, dtype=torch.int32, device=DEV) if fp8 else None
+        scf = sc.view(torch.float32) if fp8 else None
+        if form == "chunks":
+            pat.scatter(src_d, rows_d, dst.view(torch.uint8), scf)()
+        else:
+            pat.scatter_rows(src_d, rows_d, dst.view(torch.uint8), scf)()
+        torch.cuda.synchronize()
+        outs.append((_u32(dst), None if sc is None else _u32(sc)))
+    assert np.array_equal(outs[0][0], outs[1][0])
+    if fp8:
+        assert np.array_equal(outs[0][1], outs[1][1])
+    assert np.any(outs[0][0] != 0xFFFFFFFF)
+
+
 @pytest.mark.parametrize("v", [1, 2])
 def test_gather(pat, v):
     print(f"case ceilings gather V={v}", flush=True)
