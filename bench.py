@@ -509,8 +509,9 @@ def ceiling_lib():
     L.moe_ceiling_gather.argtypes = [P, i32, i32, i32, P, i32, i32, P, P]
     L.moe_ceiling_gather_persistent.argtypes = [P, i32, i32, i32, P, i32, i32, i32, P, P]
     L.moe_ceiling_scatter_rows.argtypes = [P, i32, i32, i32, P, P, i32, P, P]
+    L.moe_ceiling_gather_policy.argtypes = [P, i32, i32, i32, P, i32, P, P]
     for f in (L.moe_ceiling_read, L.moe_ceiling_write, L.moe_ceiling_scatter, L.moe_ceiling_gather,
-              L.moe_ceiling_gather_persistent, L.moe_ceiling_scatter_rows):
+              L.moe_ceiling_gather_persistent, L.moe_ceiling_scatter_rows, L.moe_ceiling_gather_policy):
         f.restype = i32
     return L
 
@@ -571,6 +572,12 @@ class Patterns:
         sp = scales.data_ptr() if scales is not None else None
         return lambda: _checked(self.L.moe_ceiling_scatter_rows(src.data_ptr(), S, in_rb, K, rows.data_ptr(),
                                                                 dst.data_ptr(), out_rb, sp, self._s()), "scatter_rows")
+
+    def gather_policy(self, y, rows, out, policy):
+        S, K = rows.shape
+        rb = y.shape[1] * y.element_size()
+        return lambda: _checked(self.L.moe_ceiling_gather_policy(y.data_ptr(), S, rb, K, rows.data_ptr(), policy,
+                                                                 out.data_ptr(), self._s()), "gather_policy")
 
     def gather_persistent(self, y, rows, out, groups, waves, kind="sc1"):
         S, K = rows.shape
@@ -648,6 +655,9 @@ def ceiling_sweep(moe, dev, iters: int = 30):
               + torch.arange(S, device=dev, dtype=torch.int32)[:, None]).contiguous()
     ms = time_calls(pat.gather(y, planes, out, 1, "sc1"), iters, 5)
     res["gather"]["planes 1KiB/wave/sc1"] = _gbps(bg, ms)
+    for name_p, pol in (("none", 0), ("NT", 2), ("NT+SC0", 3), ("NT+SC1", 18), ("NT+SC0+SC1", 19)):
+        ms = time_calls(pat.gather_policy(y, rows, out, pol), iters, 5)
+        res["gather"][f"buffer loads {name_p}/sc1"] = _gbps(bg, ms)
     n_cu = torch.cuda.get_device_properties(dev).multi_processor_count
     for per_cu in (2, 4, 8):
         for waves in (1, 4):
@@ -700,6 +710,9 @@ def ceilings_markdown(c: dict) -> str:
                  f"{G[f'{v}KiB/wave/nt']:,.0f} | {G[f'{v}KiB/wave/sc1']:,.0f} |")
     L.append(f"| single-wave, 1 KiB, contiguous planes (row k*S+t, no routing) | — | — | "
              f"{G['planes 1KiB/wave/sc1']:,.0f} |")
+    for key in [k for k in G if k.startswith("buffer loads")]:
+        L.append(f"| single-wave, 1 KiB, gathers by buffer loads with {key.split()[2].split('/')[0]} | — | — | "
+                 f"{G[key]:,.0f} |")
     for key in sorted(k for k in G if k.startswith("persistent")):
         per_cu, w = key.split()[1], key.split()[3].lstrip("x")
         L.append(f"| persistent: {per_cu} workgroups per CU x {w} wave(s), next unit's rows in flight | — | — | "
@@ -725,6 +738,10 @@ def ceilings_markdown(c: dict) -> str:
             L.append(f"Persistent gather pattern at the {wl} shape (µs, same rows): "
                      + ", ".join(f"{k} {v}" for k, v in pers.items())
                      + f"; one single-wave workgroup per unit: {d['combine']['pattern_us']} µs.")
+        pol = d["combine"].get("load_policy_pattern_us") or {}
+        if pol:
+            L.append(f"Gather pattern at the {wl} shape by gather cache policy (buffer loads, SC1 store, µs): "
+                     + ", ".join(f"{k} {v}" for k, v in pol.items()) + ".")
         ro = d["dispatch"].get("pattern_row_order_us")
         if ro is not None:
             L.append(f"Scatter pattern at the {wl} shape in row order (a workgroup per token through LDS): {ro} µs; "
@@ -759,6 +776,11 @@ def pattern_vs_product(moe, run, dev, iters: int = 30):
     t_rows = time_calls(pat.scatter_rows(hid_u8, rows, recv_u8, run.buf.recv_scales), iters, 5)
     t_c = time_calls(run.combine_call, iters, 5)
     t_g = time_calls(gath, iters, 5)
+    pol_us = {}
+    if run.cfg.K == 8:
+        for name_p, pol in (("NT", 2), ("NT+SC0", 3), ("NT+SC1", 18), ("NT+SC0+SC1", 19)):
+            pol_us[name_p] = round(time_calls(pat.gather_policy(run.expert_out.view(torch.uint8), rows,
+                                                                run.buf.out.view(torch.uint8), pol), iters, 5) * 1e3, 2)
     n_cu = torch.cuda.get_device_properties(dev).multi_processor_count
     pers = {}
     for per_cu, waves in ((4, 1), (8, 1), (2, 4), (4, 4)):
@@ -777,7 +799,8 @@ def pattern_vs_product(moe, run, dev, iters: int = 30):
     out["combine"] = {"kernel_us": round(t_c * 1e3, 2), "pattern_us": round(t_g * 1e3, 2),
                       "pattern": "moe_ceiling_gather with the same rows, SC1 output store",
                       "kernel_gbps": _gbps(cb, t_c), "pattern_gbps": _gbps(cb, t_g),
-                      "kernel_over_pattern": round(t_g / t_c, 4), "persistent_pattern_us": pers}
+                      "kernel_over_pattern": round(t_g / t_c, 4), "persistent_pattern_us": pers,
+                      "load_policy_pattern_us": pol_us}
     out["note"] = "back-to-back launches of one kernel; bytes are the product's algorithmic bytes"
     return out
 

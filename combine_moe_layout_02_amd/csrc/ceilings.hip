@@ -171,6 +171,33 @@ __global__ __launch_bounds__(kWave) void k_gather(const u32x4 *__restrict__ y, i
     }
 }
 
+// The gather pattern with the gathers' cache-policy operand given (buffer
+// loads through a descriptor per row: bit 0 SC0, bit 1 NT, bit 4 SC1) and an
+// SC1 output store; one single-wave workgroup per (token, 1 KiB chunk).
+template <int K, int POL>
+__global__ __launch_bounds__(kWave) void k_gather_policy(const u32x4 *__restrict__ y, int nvec,
+                                                         const int32_t *__restrict__ rows, u32x4 *__restrict__ out,
+                                                         int nchunk) {
+    const int t = blockIdx.x / nchunk, c = blockIdx.x % nchunk;
+    const int32_t *pr = rows + static_cast<size_t>(t) * K;
+    int p[K];
+#pragma unroll
+    for (int k = 0; k < K; ++k) p[k] = pr[k];
+    u32x4 r[K];
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+        const u32x4 *chunk = y + static_cast<size_t>(p[k] >= 0 ? p[k] : 0) * nvec + c * kWave;
+        const __amdgpu_buffer_rsrc_t d = __builtin_amdgcn_make_buffer_rsrc(const_cast<u32x4 *>(chunk), 0,
+                                                                          p[k] >= 0 ? kWave * 16 : 0, kBufferRsrcWord3);
+        r[k] = __builtin_amdgcn_raw_buffer_load_b128(d, threadIdx.x * 16, 0, POL);
+    }
+    u32x4 x = r[0];
+#pragma unroll
+    for (int k = 1; k < K; ++k) x ^= r[k];
+    store16<STORE_SC1>(x, out + static_cast<size_t>(t) * nvec, static_cast<unsigned int>(c * kWave + threadIdx.x),
+                       static_cast<unsigned int>(nvec) * 16u);
+}
+
 // The gather pattern in persistent form: every wave walks (token, 1 KiB
 // chunk) units u = w, w + nwaves, ... (chunk-fastest, as above) and keeps the
 // next unit's K row loads in flight while it combines and stores the current
@@ -444,5 +471,27 @@ extern "C" int32_t moe_ceiling_scatter_rows(const void *src, int32_t S, int32_t 
         default: return MOE_CEIL_ERR_ARG;
     }
 #undef CEIL_SR
+    return launched();
+}
+
+extern "C" int32_t moe_ceiling_gather_policy(const void *y, int32_t S, int32_t row_bytes, int32_t K, const int32_t *rows,
+                                             int32_t load_policy, void *out, void *stream) {
+    if (y == nullptr || rows == nullptr || out == nullptr || !aligned16(y) || !aligned16(out)) return MOE_CEIL_ERR_ARG;
+    if (S < 1 || row_bytes < 1024 || row_bytes % 1024 || K != 8) return MOE_CEIL_ERR_ARG;
+    if (load_policy != 0 && load_policy != 2 && load_policy != 3 && load_policy != 18 && load_policy != 19)
+        return MOE_CEIL_ERR_ARG;
+    const int nvec = row_bytes / 16, nchunk = nvec / kWave;
+    if (static_cast<int64_t>(S) * nchunk > 0x7FFFFFFFLL) return MOE_CEIL_ERR_ARG;
+    const dim3 grid(static_cast<unsigned>(S * nchunk));
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    const u32x4 *yv = static_cast<const u32x4 *>(y);
+    u32x4 *ov = static_cast<u32x4 *>(out);
+    switch (load_policy) {
+        case 0: hipLaunchKernelGGL((k_gather_policy<8, 0>), grid, dim3(kWave), 0, st, yv, nvec, rows, ov, nchunk); break;
+        case 2: hipLaunchKernelGGL((k_gather_policy<8, 2>), grid, dim3(kWave), 0, st, yv, nvec, rows, ov, nchunk); break;
+        case 3: hipLaunchKernelGGL((k_gather_policy<8, 3>), grid, dim3(kWave), 0, st, yv, nvec, rows, ov, nchunk); break;
+        case 18: hipLaunchKernelGGL((k_gather_policy<8, 18>), grid, dim3(kWave), 0, st, yv, nvec, rows, ov, nchunk); break;
+        default: hipLaunchKernelGGL((k_gather_policy<8, 19>), grid, dim3(kWave), 0, st, yv, nvec, rows, ov, nchunk); break;
+    }
     return launched();
 }

@@ -79,6 +79,13 @@ int32_t moe_ceiling_gather(const void *y, int32_t S, int32_t row_bytes, int32_t 
 int32_t moe_ceiling_scatter_rows(const void *src, int32_t S, int32_t in_row_bytes, int32_t K, const int32_t *rows,
                                  void *dst, int32_t out_row_bytes, float *scales, void *stream);
 
+/* The combine pattern with the gathers' cache-policy operand given:
+ * load_policy is the buffer load's operand (0 none, 2 NT, 3 NT+SC0, 18 NT+SC1,
+ * 19 NT+SC0+SC1); the output store carries SC1.  Same output as
+ * moe_ceiling_gather (vec_per_lane 1).  K = 8. */
+int32_t moe_ceiling_gather_policy(const void *y, int32_t S, int32_t row_bytes, int32_t K, const int32_t *rows,
+                                  int32_t load_policy, void *out, void *stream);
+
 /* The combine pattern in persistent form: `groups` workgroups of
  * waves_per_group waves (1..4) walk the same (token, 1 KiB chunk) units as
  * moe_ceiling_gather (chunk-fastest), each wave keeping the next unit's K row

@@ -179,8 +179,8 @@ def test_ceiling_library_exports_and_rejects_bad_arguments():
         __graft_entry__.build()
     text = re.sub(r"/\*.*?\*/", "", open(CEIL_HEADER).read(), flags=re.S)
     names = sorted(set(re.findall(r"\b(moe_ceiling_[a-z_0-9]+)\s*\(", text)))
-    assert names == ["moe_ceiling_gather", "moe_ceiling_gather_persistent", "moe_ceiling_read", "moe_ceiling_scatter",
-                     "moe_ceiling_scatter_rows", "moe_ceiling_write"]
+    assert names == ["moe_ceiling_gather", "moe_ceiling_gather_persistent", "moe_ceiling_gather_policy",
+                     "moe_ceiling_read", "moe_ceiling_scatter", "moe_ceiling_scatter_rows", "moe_ceiling_write"]
     import bench
     L = bench.ceiling_lib()
     for n in names:
@@ -225,3 +225,12 @@ def test_ceiling_scatter_rows_rejects_bad_arguments():
     assert L.moe_ceiling_scatter_rows(P(A), 8, 2048, 7, P(A), P(A), 1024, None, None) == 1       # K = 7
     assert L.moe_ceiling_scatter_rows(P(A), 8, 3072, 8, P(A), P(A), 1024, None, None) == 1       # row ratio
     assert L.moe_ceiling_scatter_rows(P(A), 8, 131072, 8, P(A), P(A), 131072, None, None) == 1   # row > 64 KiB
+
+
+def test_ceiling_gather_policy_rejects_bad_arguments():
+    import bench
+    L = bench.ceiling_lib()
+    P = ctypes.c_void_p
+    A = FAKE
+    assert L.moe_ceiling_gather_policy(P(A), 8, 1024, 8, P(A), 1, P(A), None) == 1    # policy 1 not swept
+    assert L.moe_ceiling_gather_policy(P(A), 8, 1024, 6, P(A), 2, P(A), None) == 1    # K = 6

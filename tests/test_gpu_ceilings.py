@@ -154,3 +154,24 @@ def test_gather_persistent(pat, groups, waves):
                               groups, waves, kind)()
         torch.cuda.synchronize()
         assert np.array_equal(_u32(out), want), kind
+
+
+@pytest.mark.parametrize("policy", [0, 2, 3, 18, 19])
+def test_gather_policy(pat, policy):
+    print(f"case ceilings gather policy={policy}", flush=True)
+    S, K, rb = 7, 8, 2048
+    rng = np.random.default_rng(8)
+    nrows = 60
+    y = rng.integers(0, 2 ** 32, (nrows, rb // 4), dtype=np.uint64).astype(np.uint32)
+    rows = rng.integers(0, nrows, (S, K)).astype(np.int32)
+    rows[2, 6] = -1
+    want = np.zeros((S, rb // 4), np.uint32)
+    for t in range(S):
+        for k in range(K):
+            if rows[t, k] >= 0:
+                want[t] ^= y[rows[t, k]]
+    out = torch.full((S, rb // 4), -1, dtype=torch.int32, device=DEV)
+    pat.gather_policy(torch.from_numpy(y.view(np.int32)).to(DEV).view(torch.uint8), torch.from_numpy(rows).to(DEV),
+                      out.view(torch.uint8), policy)()
+    torch.cuda.synchronize()
+    assert np.array_equal(_u32(out), want)
