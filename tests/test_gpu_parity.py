@@ -909,3 +909,94 @@ def test_layout_random_sweep(moe):
         for k in ("tokens_per_expert", "tokens_per_rank", "expert_offset", "rank_offset", "pos", "src", "status"):
             want = getattr(ref, k)
             assert np.array_equal(getattr(lay_b, k).cpu().numpy().reshape(want.shape), want), f"{case}: balanced {k}"
+
+
+BEYOND_4GIB = [
+    # bf16 rows of 14 KiB with padding: an 8.0 GB receive buffer (its last row
+    # at byte 7.98e9), also read back by combine as the expert outputs
+    (WorkloadConfig("beyond4g-bf16", S=65536, H=7168, E=256, K=8, R=8, routing="uniform",
+                    pad_mode=PAD_MULTIPLE, pad_rows=128), False),
+    # FP8 rows of 4,224 bytes: a 4.43 GB receive buffer, 1,048,576 entries
+    # (the two-launch layout with its largest tiles)
+    (WorkloadConfig("beyond4g-fp8", S=131072, H=4224, E=64, K=8, R=8, routing="uniform"), True),
+]
+
+
+@pytest.mark.parametrize("case", BEYOND_4GIB, ids=[c[0].name for c in BEYOND_4GIB])
+def test_beyond_4gib(moe, case):
+    """Receive buffers larger than 4 GiB: the whole layout bit-exact against
+    the oracle, and sampled tokens -- random ones, the owners of the highest
+    rows and of the rows around the 4 GiB byte boundary -- dispatched (and for
+    bf16 combined from the receive buffer) exactly as the oracle computes them
+    for those tokens alone.  Padding rows near the end must stay untouched."""
+    from workloads import softmax_weights, stamped_rows_bf16_bits, uniform_distinct_routing
+    cfg, fp8 = case
+    S, H, E, K, R = cfg.S, cfg.H, cfg.E, cfg.K, cfg.R
+    say(f"case {cfg.name}: S={S} H={H} E={E} K={K} fp8={fp8}")
+    rng = np.random.default_rng(77)
+    idx = uniform_distinct_routing(rng, S, E, K)
+    w = softmax_weights(rng.standard_normal((S, K), dtype=np.float32))
+    hidden = stamped_rows_bf16_bits(78, S, H)
+    desc = moe.LayoutDesc(S, K, E, R, cfg.pad_mode, cfg.pad_rows)
+    rows = moe.moe_max_recv_rows(desc)
+    row_bytes = H if fp8 else 2 * H
+    assert rows * row_bytes > (1 << 32)
+    ref = oracle.layout(idx, E, R, cfg.pad_mode, cfg.pad_rows)
+    assert rows == len(ref.src)
+
+    idx_d = torch.from_numpy(idx).to(DEV)
+    w_d = torch.from_numpy(w).to(DEV)
+    hid_d = dev_bf16(hidden, DEV)
+    lay = moe.moe_layout(desc, idx_d)
+    torch.cuda.synchronize()
+    compare_layout(lay, ref, f"{cfg.name} layout")
+    say("  layout ok")
+
+    if fp8:
+        recv = torch.full((rows, H), POISON_U8, dtype=torch.uint8, device=DEV)
+        scales = torch.full((rows, H // 128), float("nan"), dtype=torch.float32, device=DEV)
+    else:
+        recv = torch.full((rows, H), POISON_BF16, dtype=torch.int16, device=DEV).view(torch.bfloat16)
+        scales = None
+    recv_w = torch.full((rows,), float("nan"), dtype=torch.float32, device=DEV)
+    moe.moe_dispatch(desc, lay, hid_d, idx_d, w_d, fp8=fp8, recv=recv, recv_scales=scales, recv_w=recv_w)
+    torch.cuda.synchronize()
+
+    flat = ref.pos.reshape(-1)
+    by_row = np.argsort(flat)
+    boundary = (1 << 32) // row_bytes           # the row that straddles byte 2**32
+    near = np.nonzero(np.abs(flat.astype(np.int64) - boundary) <= 2)[0]
+    tokens = np.unique(np.concatenate([rng.choice(S, 384, replace=False), by_row[-64:] // K, near // K,
+                                       [0, S - 1]]))
+    assert int(flat[by_row[-1]]) * row_bytes > (1 << 32) and near.size > 0
+    n = tokens.size
+    pos_sub = np.arange(n * K, dtype=np.int32).reshape(n, K)
+    sel = ref.pos[tokens].reshape(-1)
+    recv_host = recv.view(torch.uint8) if fp8 else recv.view(torch.int16)
+    got = np.stack([recv_host[int(r)].cpu().numpy() for r in sel])
+    got_w = recv_w.cpu().numpy()[sel]
+    if fp8:
+        want, want_s, want_w = oracle.dispatch_fp8(hidden[tokens], pos_sub, n * K, w[tokens])
+        got_s = np.stack([scales[int(r)].cpu().numpy() for r in sel])
+        assert np.array_equal(got, want), "fp8 codes differ"
+        assert np.array_equal(got_s.view(np.uint32), want_s.view(np.uint32)), "fp8 scales differ"
+    else:
+        want, want_w = oracle.dispatch_bf16(hidden[tokens], pos_sub, n * K, w[tokens])
+        assert np.array_equal(got.view(np.uint16), want), "bf16 rows differ"
+    assert np.array_equal(got_w.view(np.uint32), want_w.view(np.uint32)), "recv_w differs"
+    pad_rows = np.nonzero(ref.src < 0)[0][-64:]
+    for r in pad_rows:
+        row = recv_host[int(r)].cpu().numpy()
+        assert np.all(row.view(np.uint8 if fp8 else np.uint16) == (POISON_U8 if fp8 else POISON_BF16)), r
+    say(f"  dispatch ok on {n} sampled tokens ({n * K} rows, last row {int(flat[by_row[-1]])}), "
+        f"{pad_rows.size} padding rows untouched")
+
+    if not fp8:
+        out = moe.moe_combine(desc, lay, recv, w_d)
+        torch.cuda.synchronize()
+        got_o = host_bits(out[torch.from_numpy(tokens).to(DEV)])
+        assert_combine_matches(got_o, oracle.combine(want, pos_sub, w[tokens]), "combine beyond 4 GiB")
+        say("  combine ok")
+        del out
+    del recv, scales, recv_w, hid_d, lay
+    torch.cuda.empty_cache()

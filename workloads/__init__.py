@@ -13,6 +13,7 @@ from .gen import (  # noqa: F401
     make_workload,
     normal_bf16_bits,
     random_expert_out_bits,
+    stamped_rows_bf16_bits,
     uniform_distinct_routing,
     group_limited_routing,
     zipf_routing,

@@ -34,6 +34,7 @@ _TAG_WEIGHTS = 3
 _TAG_SHARED_A = 4
 _TAG_SHARED_B = 5
 _TAG_EXPERT_OUT = 6
+_TAG_STAMPED = 7
 
 
 @dataclasses.dataclass(frozen=True)
@@ -218,4 +219,28 @@ def random_expert_out_bits(seed: int, rows: int, H: int,
     else:
         sel = np.nonzero(row_mask)[0]
         out[sel] = normal_bf16_bits(rng, (sel.size, H))
+    return out
+
+
+def stamped_rows_bf16_bits(seed: int, S: int, H: int, base_rows: int = 1024) -> np.ndarray:
+    """Token rows [S, H] bf16 bits for batches too large to draw row by row:
+    row t is row t % base_rows of an N(0,1) table, and in every 512-channel
+    chunk c the first four channels hold the small integers t & 255,
+    (t >> 8) & 255, t >> 16 and c & 255 (exact in bf16), so a row or a chunk
+    that lands in another token's or chunk's place cannot match.  H must be a
+    multiple of 8 and S < 2**24."""
+    if H % 8 or not 0 <= S < (1 << 24):
+        raise ValueError("H must be a multiple of 8 and S < 2**24")
+    base = normal_bf16_bits(_rng(seed, _TAG_STAMPED), (base_rows, H))
+    out = np.empty((S, H), dtype=np.uint16)
+    for i in range(0, S, base_rows):
+        n = min(base_rows, S - i)
+        out[i:i + n] = base[:n]
+    small = (np.arange(256, dtype=np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    t = np.arange(S)
+    for c, col in enumerate(range(0, H, 512)):
+        out[:, col] = small[t & 255]
+        out[:, col + 1] = small[(t >> 8) & 255]
+        out[:, col + 2] = small[t >> 16]
+        out[:, col + 3] = small[c & 255]
     return out
