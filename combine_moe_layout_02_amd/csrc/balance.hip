@@ -429,18 +429,30 @@ __global__ __launch_bounds__(kLayoutThreads) void k_layout_balanced_onepass(Layo
     const int base = tb * kLayoutThreads + wave * kWave;
     int raw[1];
     load_keys<1>(a.idx, a.N, base, raw);
+    // the other tiles' entries, loaded before anything else when idx allows
+    // 16-byte loads (one batch covers every one-launch size)
+    const bool issued = (reinterpret_cast<uintptr_t>(a.idx) & 15u) == 0;
+    int4 q[kOtherBatch];
+    int nbad = 0;
+    if (issued) other_issue(a.idx, a.N, tb, 0, q, nbad);
     for (int x = tid; x < kLayoutWaves * E; x += kLayoutThreads) s_cnt[x] = 0;
     other_clear(s_part, E);
     if (tid == 0) {
         s_bad = 0;
         L.flags = 0;
     }
-    __syncthreads();
+    lds_barrier();  // the loads above stay in flight
+    // nothing that reads the own key may move above the barrier: a use
+    // there makes the wave wait for every load issued before it
+    asm volatile("" : "+v"(raw[0]));
 
     int flags = 0, bad = 0;
     int key[1], local[1];
-    count_other_tiles(a.idx, a.N, E, nblk, tb, s_part, flags, bad,
-                      [&] { wave_rank<1>(raw, a.N, E, a.nbits, base, s_cnt + wave * E, key, local, flags); });
+    const auto rank_own = [&] { wave_rank<1>(raw, a.N, E, a.nbits, base, s_cnt + wave * E, key, local, flags); };
+    if (issued)
+        count_other_tiles_issued(q, a.N, E, tb, s_part, nbad, flags, bad, rank_own);
+    else
+        count_other_tiles(a.idx, a.N, E, nblk, tb, s_part, flags, bad, rank_own);
     if (base + lane < a.N && key[0] < 0) ++bad;
     if (flags) atomicOr(&L.flags, flags);
     if (bad) atomicAdd(&s_bad, bad);

@@ -125,6 +125,15 @@ __device__ __forceinline__ u32x4 quantize16_e4m3(u32x4 lo, u32x4 hi, float &scal
     return q;
 }
 
+// Workgroup barrier that orders LDS accesses only.  __syncthreads also waits
+// for every global load the wave has in flight; this one lets them stay in
+// flight across the barrier.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // Number of set bits of `m` below this lane (v_mbcnt_lo / v_mbcnt_hi).
 __device__ __forceinline__ int lanes_below(uint64_t m) {
     return __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(m >> 32),
@@ -263,11 +272,61 @@ __device__ __forceinline__ void other_clear(unsigned int *s_part, int E) {
     for (int x = threadIdx.x; x < ((E + 1) << other_copies_log2(E)); x += kLayoutThreads) s_part[x] = 0u;
 }
 
-// count_other_tiles with 1 << CL copies (a constant, so the counter address is
-// one shift-and-or).  An id outside [0,E) adds one to nbad and is counted into
-// the spare expert E, which nothing reads, so every lane takes part in every
-// atomic and the loop has no branches per entry; slots past N are loaded as -1
-// and taken back out of nbad.
+// The aligned count reads rounds of 4 * 1024 entries, thread tid entries
+// 4*tid .. 4*tid+3 of each round with one 16-byte load, kOtherBatch rounds in
+// flight; one batch covers every batch the one-launch layouts take.
+constexpr int kOtherGroup = 4 * kLayoutThreads;
+constexpr int kOtherBatch = 8;
+static_assert(kOnePassMaxN <= kOtherGroup * kOtherBatch, "one batch of loads covers a one-launch layout");
+
+// Issues the loads of rounds g0 .. g0 + kOtherBatch - 1 that lie outside tile
+// b (idx 16-byte aligned).  Slots past N are loaded as -1 and taken back out
+// of nbad here.
+__device__ __forceinline__ void other_issue(const int32_t *__restrict__ idx, int N, int b, int g0,
+                                            int4 (&q)[kOtherBatch], int &nbad) {
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int u = 0; u < kOtherBatch; ++u) {
+        const int i = (g0 + u) * kOtherGroup + 4 * tid;
+        if (i + 3 < N && i / kLayoutThreads != b) {
+            q[u] = *reinterpret_cast<const int4 *>(idx + i);
+        } else if (i < N && i / kLayoutThreads != b) {  // the ragged end of the batch
+            q[u].x = idx[i];
+            q[u].y = i + 1 < N ? idx[i + 1] : -1;
+            q[u].z = i + 2 < N ? idx[i + 2] : -1;
+            q[u].w = -1;
+            nbad -= i + 4 - N;
+        }
+    }
+}
+
+// Adds what other_issue loaded into the packed counters (1 << CL copies, a
+// constant, so the counter address is one shift-and-or).  An id outside
+// [0,E) adds one to nbad and is counted into the spare expert E, which
+// nothing reads, so every lane takes part in every atomic and the loop has no
+// branches per entry.
+template <int CL>
+__device__ __forceinline__ void other_add(const int4 (&q)[kOtherBatch], int N, int E, int b, int g0,
+                                          unsigned int *s_part, int &nbad) {
+    const int tid = threadIdx.x;
+    unsigned int *__restrict__ part = s_part + (tid & ((1 << CL) - 1));
+    const unsigned int uE = static_cast<unsigned>(E);
+#pragma unroll
+    for (int u = 0; u < kOtherBatch; ++u) {
+        const int i = (g0 + u) * kOtherGroup + 4 * tid, t = i / kLayoutThreads;
+        if (i >= N || t == b) continue;
+        const unsigned int inc = t < b ? 0x10001u : 1u;
+        const int e4[4] = {q[u].x, q[u].y, q[u].z, q[u].w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const bool ok = static_cast<unsigned>(e4[j]) < uE;
+            nbad += ok ? 0 : 1;
+            atomicAdd(part + ((ok ? e4[j] : E) << CL), inc);
+        }
+    }
+}
+
+// count_other_tiles with 1 << CL copies.
 template <int CL, typename Between>
 __device__ __forceinline__ void count_other_tiles_cl(const int32_t *__restrict__ idx, int N, int E, int nblk, int b,
                                                      unsigned int *s_part, int &nbad, Between &&between) {
@@ -279,37 +338,11 @@ __device__ __forceinline__ void count_other_tiles_cl(const int32_t *__restrict__
         return;
     }
     if ((reinterpret_cast<uintptr_t>(idx) & 15u) == 0) {
-        constexpr int kGroup = 4 * kLayoutThreads;  // entries per round of 16-byte loads
-        constexpr int kBatch = 8;
-        for (int g0 = 0; g0 * kGroup < N; g0 += kBatch) {
-            int4 q[kBatch];
-#pragma unroll
-            for (int u = 0; u < kBatch; ++u) {
-                const int i = (g0 + u) * kGroup + 4 * tid;
-                if (i + 3 < N && i / kLayoutThreads != b) {
-                    q[u] = *reinterpret_cast<const int4 *>(idx + i);
-                } else if (i < N && i / kLayoutThreads != b) {  // the ragged end of the batch
-                    q[u].x = idx[i];
-                    q[u].y = i + 1 < N ? idx[i + 1] : -1;
-                    q[u].z = i + 2 < N ? idx[i + 2] : -1;
-                    q[u].w = -1;
-                    nbad -= i + 4 - N;
-                }
-            }
+        for (int g0 = 0; g0 * kOtherGroup < N; g0 += kOtherBatch) {
+            int4 q[kOtherBatch];
+            other_issue(idx, N, b, g0, q, nbad);
             if (g0 == 0) between();
-#pragma unroll
-            for (int u = 0; u < kBatch; ++u) {
-                const int i = (g0 + u) * kGroup + 4 * tid, t = i / kLayoutThreads;
-                if (i >= N || t == b) continue;
-                const unsigned int inc = t < b ? 0x10001u : 1u;
-                const int e4[4] = {q[u].x, q[u].y, q[u].z, q[u].w};
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const bool ok = static_cast<unsigned>(e4[j]) < uE;
-                    nbad += ok ? 0 : 1;
-                    atomicAdd(part + ((ok ? e4[j] : E) << CL), inc);
-                }
-            }
+            other_add<CL>(q, N, E, b, g0, s_part, nbad);
         }
     } else {
         // idx not 16-byte aligned: entry t*1024 + tid of every tile t, 16 loads in flight
@@ -358,6 +391,26 @@ __device__ __forceinline__ void count_other_tiles(const int32_t *__restrict__ id
         count_other_tiles_cl<2>(idx, N, E, nblk, b, s_part, nbad, between);
     else
         count_other_tiles_cl<1>(idx, N, E, nblk, b, s_part, nbad, between);
+    if (nbad) flags |= FLAG_BAD_EXPERT;
+    bad += nbad;
+}
+
+// count_other_tiles for a one-launch layout whose loads other_issue already
+// issued (round 0 on, idx 16-byte aligned): the caller issues them before it
+// clears its counters, so their latency overlaps that work and its first
+// barrier.  `between()` runs before the first count, as in count_other_tiles.
+template <typename Between>
+__device__ __forceinline__ void count_other_tiles_issued(const int4 (&q)[kOtherBatch], int N, int E, int b,
+                                                         unsigned int *s_part, int nbad, int &flags, int &bad,
+                                                         Between &&between) {
+    between();
+    const int cl = other_copies_log2(E);
+    if (cl == 3)
+        other_add<3>(q, N, E, b, 0, s_part, nbad);
+    else if (cl == 2)
+        other_add<2>(q, N, E, b, 0, s_part, nbad);
+    else
+        other_add<1>(q, N, E, b, 0, s_part, nbad);
     if (nbad) flags |= FLAG_BAD_EXPERT;
     bad += nbad;
 }
